@@ -1,0 +1,145 @@
+"""Pins of the oracle's block-scaled GEMM and grouped GEMM against
+hand-worked cases, exact rational arithmetic, integer matmul and
+composition identities."""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from fp8_fine_grained_fp8bs_amd import synth
+from tests.exact_ref import torch_e4m3_table
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+TAB = torch_e4m3_table()
+
+
+def _rle(runs):
+    return np.concatenate([np.full(n, c, np.uint8) for c, n in runs])
+
+
+def test_gemm_hand_cases():
+    cases = json.load(open(os.path.join(GOLDEN, "gemm_hand.json")))["cases"]
+    for case in cases:
+        a = _rle(case["a"])[None, :]
+        b = _rle(case["b"])[None, :]
+        sa = np.array([case["sa"]], np.float32)
+        sb = np.array([case["sb"]], np.float32)
+        for mode in (oracle.BSCALE_BLOCK, oracle.BSCALE_ROW):
+            d = oracle.gemm(a, sa, b, sb, mode)
+            assert d[0, 0] == case["d"], case["note"]
+
+
+def _rand_codes(rng, shape):
+    c = rng.integers(0, 256, shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x3A
+    return c
+
+
+def _rand_scales(rng, shape):
+    return (rng.uniform(0.5, 2.0, shape) * 2.0 ** rng.integers(-30, 30, shape)).astype(np.float32)
+
+
+def test_gemm_exact_rational_small_shapes():
+    rng = np.random.default_rng(2)
+    for (M, N, K) in [(1, 1, 128), (3, 2, 256), (2, 4, 384), (4, 3, 128)]:
+        a = _rand_codes(rng, (M, K)); b = _rand_codes(rng, (N, K))
+        sa = _rand_scales(rng, (M, K // 128))
+        for mode in (oracle.BSCALE_BLOCK, oracle.BSCALE_ROW):
+            sb = _rand_scales(rng, (1 if mode == 0 else N, K // 128))
+            d = oracle.gemm(a, sa, b, sb, mode)
+            for m in range(M):
+                for n in range(N):
+                    exact = Fraction(0)
+                    mag = Fraction(0)
+                    for k in range(K):
+                        g = k // 128
+                        sbv = sb[0 if mode == 0 else n, g]
+                        t = (Fraction(float(TAB[a[m, k]])) * Fraction(float(sa[m, g])) *
+                             Fraction(float(TAB[b[n, k]])) * Fraction(float(sbv)))
+                        exact += t
+                        mag += abs(t)
+                    err = abs(Fraction(d[m, n]) - exact)
+                    assert err <= 2 * K * Fraction(2) ** -53 * mag, (M, N, K, m, n)
+
+
+def test_gemm_integer_codes_equal_int_matmul():
+    rng = np.random.default_rng(4)
+    M, N, K = 24, 40, 384
+    ia = rng.integers(-16, 17, (M, K)); ib = rng.integers(-16, 17, (N, K))
+    import torch
+    enc = lambda v: torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    a, b = enc(ia), enc(ib)
+    assert np.array_equal(TAB[a], ia) and np.array_equal(TAB[b], ib)
+    sa = np.ones((M, 3), np.float32); sb = np.ones((1, 3), np.float32)
+    d = oracle.gemm(a, sa, b, sb)
+    assert np.array_equal(d, (ia.astype(np.int64) @ ib.T.astype(np.int64)).astype(np.float64))
+
+
+def test_gemm_scale_linearity_and_block_vs_row():
+    q = synth.tiny(M=40, N=200, K=384)
+    qa, sa = oracle.quant_act_1x128(q["A"])
+    qb, sb = oracle.quant_w_128x128(q["W"])
+    d = oracle.gemm(qa, sa, qb, sb)
+    # doubling every scale of group 1 of A adds exactly group 1's share again
+    sa2 = sa.copy(); sa2[:, 1] *= 2
+    only1 = np.zeros_like(sa); only1[:, 1] = sa[:, 1]
+    d2 = oracle.gemm(qa, sa2, qb, sb)
+    d1 = oracle.gemm(qa, only1, qb, sb)
+    scale = np.abs(oracle.gemm(qa, np.abs(sa), qb, np.abs(sb))) + 1e-300
+    assert np.all(np.abs(d2 - (d + d1)) <= 1e-12 * (np.abs(d) + np.abs(d1) + 1e-30) + 1e-14 * scale)
+    # BLOCK mode == ROW mode with the block scale broadcast over its rows
+    sb_rows = np.repeat(sb, 128, axis=0)[:200]
+    assert np.array_equal(oracle.gemm(qa, sa, qb, np.ascontiguousarray(sb_rows), oracle.BSCALE_ROW), d)
+    # a transposed operand gives a different (non-square) answer
+    assert d.shape == (40, 200)
+
+
+def test_gemm_entries_match_full():
+    q = synth.tiny(M=64, N=256, K=512)
+    qa, sa = oracle.quant_act_1x128(q["A"])
+    qb, sb = oracle.quant_w_128x128(q["W"])
+    d = oracle.gemm(qa, sa, qb, sb)
+    rng = np.random.default_rng(0)
+    mi = rng.integers(0, 64, 500); ni = rng.integers(0, 256, 500)
+    assert np.array_equal(oracle.gemm_entries(qa, sa, qb, sb, mi, ni), d[mi, ni])
+
+
+def test_grouped_gemm_is_per_expert_concat_with_empty_expert():
+    rng = np.random.default_rng(9)
+    E, N, K = 4, 192, 256
+    counts = np.array([5, 0, 130, 1])
+    off = synth.offsets_from_counts(counts)
+    T = int(off[-1])
+    a = _rand_codes(rng, (T, K)); sa = _rand_scales(rng, (T, 2))
+    b = _rand_codes(rng, (E, N, K)); sb = _rand_scales(rng, (E, 2, 2))
+    d = oracle.grouped_gemm(a, sa, b, sb, off)
+    for e in range(E):
+        r0, r1 = off[e], off[e + 1]
+        if r1 > r0:
+            de = oracle.gemm(a[r0:r1], sa[r0:r1], b[e], sb[e])
+            assert np.array_equal(d[r0:r1], de)
+    # rows of expert 2 do not depend on other experts' data
+    b2 = b.copy(); b2[0] ^= 0x01; b2[3] ^= 0x01
+    d2 = oracle.grouped_gemm(a, sa, b2, sb, off)
+    assert np.array_equal(d2[off[2]:off[3]], d[off[2]:off[3]])
+    assert not np.array_equal(d2[off[0]:off[1]], d[off[0]:off[1]])
+    mi = rng.integers(0, T, 300); ni = rng.integers(0, N, 300)
+    assert np.array_equal(oracle.grouped_gemm_entries(a, sa, b, sb, off, mi, ni), d[mi, ni])
+
+
+def test_bf16_gemm_references():
+    """The unquantized binary64 GEMM and the FP32-accumulating BF16 GEMM
+    agree within FP32 accumulation error on a small case; the binary64 one
+    equals an exact rational sum at the 2^-53 level."""
+    q = synth.probe(M=8, N=8, K=256)
+    d64 = oracle.gemm_bf16_f64(q["A"], q["W"])
+    d32 = oracle.gemm_bf16_f32acc(q["A"], q["W"])
+    xa = synth.bf16_to_f32(q["A"]).astype(np.float64)
+    xw = synth.bf16_to_f32(q["W"]).astype(np.float64)
+    mag = np.abs(xa) @ np.abs(xw).T
+    assert np.all(np.abs(d32 - d64) <= 256 * 2.0 ** -24 * mag)
+    m, n = 3, 5
+    exact = sum(Fraction(float(xa[m, k])) * Fraction(float(xw[n, k])) for k in range(256))
+    assert abs(Fraction(d64[m, n]) - exact) <= 512 * Fraction(2) ** -53 * Fraction(mag[m, n])
