@@ -1,0 +1,176 @@
+// api.hip -- the C ABI of libfp8bs: host-side argument checks and dispatch.
+//
+// Every check runs before the first HIP call, so a rejected call touches no
+// device state.  Only after the checks pass is the current device queried
+// (once per device, cached) and the kernel enqueued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "fp8bs.h"
+#include "fp8bs_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other architecture
+std::atomic<int> g_dev_state[kMaxDevices];
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+fp8bs_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return FP8BS_ERR_NO_DEVICE;
+  }
+  if (dev >= kMaxDevices) return FP8BS_ERR_NO_DEVICE;
+  int st = g_dev_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return FP8BS_ERR_NO_DEVICE;
+    }
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? FP8BS_OK : FP8BS_ERR_NO_DEVICE;
+}
+
+fp8bs_status launched(hipError_t e) {
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return FP8BS_ERR_LAUNCH;
+  }
+  return FP8BS_OK;
+}
+
+// Common checks of a row-major operand: stride and alignment.
+fp8bs_status check_matrix(const void* p, int64_t cols, int64_t ld, int64_t elem_bytes) {
+  if (p == nullptr) return FP8BS_ERR_INVALID_ARG;
+  if (ld < cols) return FP8BS_ERR_INVALID_ARG;
+  if (!aligned(p, 16) || (ld * elem_bytes) % 16 != 0) return FP8BS_ERR_MISALIGNED;
+  return FP8BS_OK;
+}
+
+fp8bs_status check_scales(const float* p, int64_t cols, int64_t ld) {
+  if (p == nullptr) return FP8BS_ERR_INVALID_ARG;
+  if (ld < cols) return FP8BS_ERR_INVALID_ARG;
+  if (!aligned(p, 4)) return FP8BS_ERR_MISALIGNED;
+  return FP8BS_OK;
+}
+
+#define FP8BS_TRY(expr)                 \
+  do {                                  \
+    fp8bs_status _s = (expr);           \
+    if (_s != FP8BS_OK) return _s;      \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8bs_status_string(fp8bs_status st) {
+  switch (st) {
+    case FP8BS_OK: return "FP8BS_OK";
+    case FP8BS_ERR_INVALID_ARG: return "FP8BS_ERR_INVALID_ARG";
+    case FP8BS_ERR_UNSUPPORTED_SHAPE: return "FP8BS_ERR_UNSUPPORTED_SHAPE";
+    case FP8BS_ERR_MISALIGNED: return "FP8BS_ERR_MISALIGNED";
+    case FP8BS_ERR_NO_DEVICE: return "FP8BS_ERR_NO_DEVICE";
+    case FP8BS_ERR_LAUNCH: return "FP8BS_ERR_LAUNCH";
+  }
+  return "FP8BS_ERR_UNKNOWN";
+}
+
+int fp8bs_version(void) { return 100; }
+
+fp8bs_status fp8bs_quant_act_1x128(const void* x, int64_t M, int64_t K, int64_t ldx,
+                                   uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                   void* stream) {
+  if (M < 0 || K <= 0) return FP8BS_ERR_INVALID_ARG;
+  if (K % 128 != 0) return FP8BS_ERR_UNSUPPORTED_SHAPE;
+  if (M == 0) return FP8BS_OK;
+  FP8BS_TRY(check_matrix(x, K, ldx, 2));
+  FP8BS_TRY(check_matrix(q, K, ldq, 1));
+  FP8BS_TRY(check_scales(s, K / 128, lds));
+  FP8BS_TRY(check_device());
+  return launched(fp8bs::launch_quant_act_1x128(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq,
+                                                s, lds, static_cast<hipStream_t>(stream)));
+}
+
+fp8bs_status fp8bs_quant_w_128x128(const void* w, int64_t N, int64_t K, int64_t ldw,
+                                   uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                   void* stream) {
+  if (N < 0 || K <= 0) return FP8BS_ERR_INVALID_ARG;
+  if (K % 128 != 0) return FP8BS_ERR_UNSUPPORTED_SHAPE;
+  if (N == 0) return FP8BS_OK;
+  FP8BS_TRY(check_matrix(w, K, ldw, 2));
+  FP8BS_TRY(check_matrix(q, K, ldq, 1));
+  FP8BS_TRY(check_scales(s, K / 128, lds));
+  FP8BS_TRY(check_device());
+  return launched(fp8bs::launch_quant_w_128x128(static_cast<const uint16_t*>(w), N, K, ldw, q, ldq,
+                                                s, lds, static_cast<hipStream_t>(stream)));
+}
+
+fp8bs_status fp8bs_requant_T_128x1(fp8bs_requant_src src, const void* in, const float* s_in,
+                                   int64_t T, int64_t C, int64_t ld_in, int64_t lds_in,
+                                   uint8_t* q_out, int64_t ld_out, float* s_out, int64_t lds_out,
+                                   void* stream) {
+  if (src != FP8BS_SRC_FP8_1x128 && src != FP8BS_SRC_BF16) return FP8BS_ERR_INVALID_ARG;
+  if (T < 0 || C <= 0) return FP8BS_ERR_INVALID_ARG;
+  if (C % 128 != 0) return FP8BS_ERR_UNSUPPORTED_SHAPE;
+  if (T == 0) return FP8BS_OK;
+  const bool bf16 = (src == FP8BS_SRC_BF16);
+  FP8BS_TRY(check_matrix(in, C, ld_in, bf16 ? 2 : 1));
+  if (!bf16) FP8BS_TRY(check_scales(s_in, C / 128, lds_in));
+  FP8BS_TRY(check_matrix(q_out, T, ld_out, 1));
+  FP8BS_TRY(check_scales(s_out, (T + 127) / 128, lds_out));
+  FP8BS_TRY(check_device());
+  return launched(fp8bs::launch_requant_T_128x1(bf16, in, s_in, T, C, ld_in, lds_in, q_out, ld_out,
+                                                s_out, lds_out, static_cast<hipStream_t>(stream)));
+}
+
+fp8bs_status fp8bs_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa,
+                        const uint8_t* b, const float* sb, int64_t ldb, int64_t ldsb,
+                        fp8bs_bscale bmode, void* d, int64_t ldd, fp8bs_out_dtype dt,
+                        int64_t M, int64_t N, int64_t K, void* stream) {
+  if (bmode != FP8BS_BSCALE_BLOCK_128x128 && bmode != FP8BS_BSCALE_ROW_1x128)
+    return FP8BS_ERR_INVALID_ARG;
+  if (dt != FP8BS_OUT_BF16 && dt != FP8BS_OUT_F32) return FP8BS_ERR_INVALID_ARG;
+  if (M < 0 || N < 0 || K <= 0) return FP8BS_ERR_INVALID_ARG;
+  if (K % 128 != 0) return FP8BS_ERR_UNSUPPORTED_SHAPE;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  FP8BS_TRY(check_matrix(a, K, lda, 1));
+  FP8BS_TRY(check_matrix(b, K, ldb, 1));
+  FP8BS_TRY(check_scales(sa, K / 128, ldsa));
+  FP8BS_TRY(check_scales(sb, K / 128, ldsb));
+  FP8BS_TRY(check_matrix(d, N, ldd, dt == FP8BS_OUT_F32 ? 4 : 2));
+  FP8BS_TRY(check_device());
+  return launched(fp8bs::launch_gemm(a, sa, lda, ldsa, b, sb, ldb, ldsb,
+                                     bmode == FP8BS_BSCALE_ROW_1x128, d, ldd, dt == FP8BS_OUT_F32,
+                                     M, N, K, static_cast<hipStream_t>(stream)));
+}
+
+fp8bs_status fp8bs_grouped_gemm(const uint8_t* a, const float* sa, int64_t ldsa,
+                                const uint8_t* b, const float* sb,
+                                const int32_t* offsets, int32_t E, int64_t M_total,
+                                void* d, fp8bs_out_dtype dt, int64_t N, int64_t K,
+                                void* stream) {
+  if (dt != FP8BS_OUT_BF16 && dt != FP8BS_OUT_F32) return FP8BS_ERR_INVALID_ARG;
+  if (E < 1 || M_total < 0 || N <= 0 || K <= 0) return FP8BS_ERR_INVALID_ARG;
+  if (K % 128 != 0) return FP8BS_ERR_UNSUPPORTED_SHAPE;
+  if (offsets == nullptr || b == nullptr || sb == nullptr) return FP8BS_ERR_INVALID_ARG;
+  if (!aligned(offsets, 4) || !aligned(sb, 4) || !aligned(b, 16)) return FP8BS_ERR_MISALIGNED;
+  if (M_total == 0) return FP8BS_OK;
+  FP8BS_TRY(check_matrix(a, K, K, 1));
+  FP8BS_TRY(check_scales(sa, K / 128, ldsa));
+  FP8BS_TRY(check_matrix(d, N, N, dt == FP8BS_OUT_F32 ? 4 : 2));
+  FP8BS_TRY(check_device());
+  return launched(fp8bs::launch_grouped_gemm(a, sa, ldsa, b, sb, offsets, E, M_total, d,
+                                             dt == FP8BS_OUT_F32, N, K,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// fp8bs_internal.h -- launchers behind the C ABI (arguments already checked).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8bs {
+
+hipError_t launch_quant_act_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                  uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                  hipStream_t st);
+
+hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                                  uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                  hipStream_t st);
+
+hipError_t launch_requant_T_128x1(bool src_bf16, const void* in, const float* s_in,
+                                  int64_t T, int64_t C, int64_t ld_in, int64_t lds_in,
+                                  uint8_t* q_out, int64_t ld_out, float* s_out,
+                                  int64_t lds_out, hipStream_t st);
+
+hipError_t launch_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa,
+                       const uint8_t* b, const float* sb, int64_t ldb, int64_t ldsb,
+                       bool bscale_row, void* d, int64_t ldd, bool out_f32,
+                       int64_t M, int64_t N, int64_t K, hipStream_t st);
+
+hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, int64_t ldsa,
+                               const uint8_t* b, const float* sb, const int32_t* offsets,
+                               int32_t E, int64_t M_total, void* d, bool out_f32,
+                               int64_t N, int64_t K, hipStream_t st);
+
+}  // namespace fp8bs

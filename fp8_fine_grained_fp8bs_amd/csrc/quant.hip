@@ -1,0 +1,151 @@
+// quant.hip -- fine-grained FP8 quantization kernels for gfx950.
+//
+// [p1] para 3 (xn--9g3bo1gtkw0l8ubf92bgle.kr post wr_id=32373): the max-abs
+// is computed online for every 1x128 activation tile and every 128x128
+// weight block, a scaling factor is derived from it and the values are
+// quantized to FP8.  Both kernels read each input byte from HBM once and
+// write each code once (the traffic the quantization round trip of [p2]
+// para 1 implies); they are HBM-bound.
+#include <hip/hip_runtime.h>
+
+#include "fp8bs_device.h"
+#include "fp8bs_internal.h"
+
+namespace fp8bs {
+namespace {
+
+// ---------------------------------------------------------------------
+// 1x128 activation tiles.  One wave per row; a 16-lane DPP row per tile,
+// 8 bf16 (16 bytes) per lane, so one wave instruction moves 4 consecutive
+// tiles (1 KiB, fully coalesced).  U tile-quads are loaded before any is
+// processed to keep enough bytes in flight.
+// ---------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                        int G, int64_t ldx, uint8_t* __restrict__ q,
+                                                        int64_t ldq, float* __restrict__ s,
+                                                        int64_t lds) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;  // uniform per wave
+  const int sub = lane & 15;
+  const int grp = lane >> 4;
+  const uint16_t* xr = x + row * ldx + sub * 8;
+  uint8_t* qr = q + row * ldq + sub * 8;
+  float* sr = s + row * lds;
+
+  for (int g0 = 0; g0 < G; g0 += 4 * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int g = g0 + 4 * u + grp;
+      if (g < G)
+        v[u] = load16_nt(xr + g * 128);
+      else
+        v[u] = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int g = g0 + 4 * u + grp;
+      float f[8] = {bf16_lo(v[u].x), bf16_hi(v[u].x), bf16_lo(v[u].y), bf16_hi(v[u].y),
+                    bf16_lo(v[u].z), bf16_hi(v[u].z), bf16_lo(v[u].w), bf16_hi(v[u].w)};
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = __builtin_fmaxf(am, __builtin_fabsf(f[i]));
+      am = row16_max(am);
+      const TileScale t = make_tile_scale(am);
+      uint2 c;
+      c.x = encode4(f, t);
+      c.y = encode4(f + 4, t);
+      if (g < G) {
+        *reinterpret_cast<uint2*>(qr + g * 128) = c;
+        if (sub == 0) sr[g] = t.s;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------
+// 128x128 weight blocks.  One 256-thread workgroup per block: thread t
+// holds rows (t>>4) + 16 i, i < 8, and the 8 bf16 at column 8 (t & 15) of
+// the block, so the whole block stays in registers between the max-abs
+// pass and the encode pass (one HBM read).  Rows past N are skipped and
+// do not enter the max-abs.
+// ---------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_w_kernel(const uint16_t* __restrict__ w, int64_t N,
+                                                      int64_t ldw, uint8_t* __restrict__ q,
+                                                      int64_t ldq, float* __restrict__ s,
+                                                      int64_t lds) {
+  __shared__ float wave_amax[4];
+  const int g = blockIdx.x;
+  const int64_t nb = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int col = (tid & 15) * 8;
+  const int r0 = tid >> 4;
+  const int64_t n0 = nb * 128;
+
+  uint4 v[8];
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t n = n0 + r0 + 16 * i;
+    if (n < N)
+      v[i] = load16_nt(w + n * ldw + static_cast<int64_t>(g) * 128 + col);
+    else
+      v[i] = make_uint4(0u, 0u, 0u, 0u);
+    am = __builtin_fmaxf(am, __builtin_fabsf(bf16_lo(v[i].x)));
+    am = __builtin_fmaxf(am, __builtin_fabsf(bf16_hi(v[i].x)));
+    am = __builtin_fmaxf(am, __builtin_fabsf(bf16_lo(v[i].y)));
+    am = __builtin_fmaxf(am, __builtin_fabsf(bf16_hi(v[i].y)));
+    am = __builtin_fmaxf(am, __builtin_fabsf(bf16_lo(v[i].z)));
+    am = __builtin_fmaxf(am, __builtin_fabsf(bf16_hi(v[i].z)));
+    am = __builtin_fmaxf(am, __builtin_fabsf(bf16_lo(v[i].w)));
+    am = __builtin_fmaxf(am, __builtin_fabsf(bf16_hi(v[i].w)));
+  }
+  am = wave_max(am);
+  if ((tid & 63) == 0) wave_amax[tid >> 6] = am;
+  __syncthreads();
+  am = __builtin_fmaxf(__builtin_fmaxf(wave_amax[0], wave_amax[1]),
+                       __builtin_fmaxf(wave_amax[2], wave_amax[3]));
+  const TileScale t = make_tile_scale(am);
+  if (tid == 0) s[nb * lds + g] = t.s;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t n = n0 + r0 + 16 * i;
+    const float f[8] = {bf16_lo(v[i].x), bf16_hi(v[i].x), bf16_lo(v[i].y), bf16_hi(v[i].y),
+                        bf16_lo(v[i].z), bf16_hi(v[i].z), bf16_lo(v[i].w), bf16_hi(v[i].w)};
+    uint2 c;
+    c.x = encode4(f, t);
+    c.y = encode4(f + 4, t);
+    if (n < N) *reinterpret_cast<uint2*>(q + n * ldq + static_cast<int64_t>(g) * 128 + col) = c;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_act_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                  uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                  hipStream_t st) {
+  const int G = static_cast<int>(K / 128);
+  const int64_t blocks = (M + 3) / 4;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  if (G % 8 == 0 && G >= 16)
+    hipLaunchKernelGGL(quant_act_kernel<2>, grid, block, 0, st, x, M, G, ldx, q, ldq, s, lds);
+  else
+    hipLaunchKernelGGL(quant_act_kernel<1>, grid, block, 0, st, x, M, G, ldx, q, ldq, s, lds);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                                  uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                  hipStream_t st) {
+  const int64_t G = K / 128;
+  const int64_t NB = (N + 127) / 128;
+  if (G > 0x7fffffff || NB > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_w_kernel, dim3(static_cast<unsigned>(G), static_cast<unsigned>(NB)),
+                     dim3(256), 0, st, w, N, ldw, q, ldq, s, lds);
+  return hipGetLastError();
+}
+
+}  // namespace fp8bs

@@ -1,0 +1,199 @@
+"""Thin ctypes binding of libfp8bs (C ABI declared in ``include/fp8bs.h``).
+
+Each ``fp8bs_*`` function has the name and argument order of the C entry
+point; tensors (PyTorch, on the GPU) stand for the device pointers and their
+row strides are taken from the tensor.  Nothing here computes: every step
+runs in the library's HIP kernels.  The ``quant_*`` / ``gemm`` helpers at the
+bottom only allocate output tensors and call the entry points.
+
+The library must have been built (``python -m fp8_fine_grained_fp8bs_amd.build``);
+loading fails loudly otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfp8bs.so")
+
+OK = 0
+ERR_INVALID_ARG = 1
+ERR_UNSUPPORTED_SHAPE = 2
+ERR_MISALIGNED = 3
+ERR_NO_DEVICE = 4
+ERR_LAUNCH = 5
+
+OUT_BF16 = 0
+OUT_F32 = 1
+BSCALE_BLOCK_128x128 = 0
+BSCALE_ROW_1x128 = 1
+SRC_FP8_1x128 = 0
+SRC_BF16 = 1
+
+ENTRY_POINTS = ("fp8bs_quant_act_1x128", "fp8bs_quant_w_128x128", "fp8bs_requant_T_128x1",
+                "fp8bs_gemm", "fp8bs_grouped_gemm", "fp8bs_status_string", "fp8bs_version")
+
+_lib = None
+
+
+class Fp8bsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def load() -> ctypes.CDLL:
+    """Load libfp8bs.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m fp8_fine_grained_fp8bs_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    sigs = {
+        "fp8bs_quant_act_1x128": [P, I64, I64, I64, P, I64, P, I64, P],
+        "fp8bs_quant_w_128x128": [P, I64, I64, I64, P, I64, P, I64, P],
+        "fp8bs_requant_T_128x1": [I, P, P, I64, I64, I64, I64, P, I64, P, I64, P],
+        "fp8bs_gemm": [P, P, I64, I64, P, P, I64, I64, I, P, I64, I, I64, I64, I64, P],
+        "fp8bs_grouped_gemm": [P, P, I64, P, P, P, I32, I64, P, I, I64, I64, P],
+    }
+    for name, args in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.fp8bs_status_string.argtypes = [ctypes.c_int]
+    lib.fp8bs_status_string.restype = ctypes.c_char_p
+    lib.fp8bs_version.argtypes = []
+    lib.fp8bs_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(st: int) -> str:
+    return load().fp8bs_status_string(int(st)).decode()
+
+
+def _ptr(t):
+    """Device pointer of a tensor (or an int address, or None for NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _ld(t):
+    """Row stride (elements) of a row-major 2-D tensor view."""
+    assert t.dim() == 2 and t.stride(1) == 1, "rows must be contiguous"
+    return t.stride(0)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _call(name, *args):
+    st = getattr(load(), name)(*args)
+    if st != OK:
+        raise Fp8bsError(st, name)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names and argument order as the C ABI)
+# ---------------------------------------------------------------------------
+
+def fp8bs_quant_act_1x128(x, q, s, stream=None):
+    """x bf16 [M][K] -> q u8 [M][K], s f32 [M][K/128]."""
+    M, K = x.shape
+    _call("fp8bs_quant_act_1x128", _ptr(x), M, K, _ld(x), _ptr(q), _ld(q), _ptr(s), _ld(s),
+          _stream(stream))
+
+
+def fp8bs_quant_w_128x128(w, q, s, stream=None):
+    """w bf16 [N][K] -> q u8 [N][K], s f32 [ceil(N/128)][K/128]."""
+    N, K = w.shape
+    _call("fp8bs_quant_w_128x128", _ptr(w), N, K, _ld(w), _ptr(q), _ld(q), _ptr(s), _ld(s),
+          _stream(stream))
+
+
+def fp8bs_requant_T_128x1(src, x, s_in, q_out, s_out, stream=None):
+    """x [T][C] (codes with s_in [T][C/128], or bf16) -> q_out [C][T],
+    s_out [C][ceil(T/128)]."""
+    T, C = x.shape
+    lds_in = _ld(s_in) if s_in is not None else 0
+    _call("fp8bs_requant_T_128x1", int(src), _ptr(x), _ptr(s_in), T, C, _ld(x), lds_in,
+          _ptr(q_out), _ld(q_out), _ptr(s_out), _ld(s_out), _stream(stream))
+
+
+def fp8bs_gemm(a, sa, b, sb, bmode, d, dt, stream=None):
+    """D [M][N] = A [M][K] * B [N][K]^T with block scales."""
+    M, K = a.shape
+    N = b.shape[0]
+    _call("fp8bs_gemm", _ptr(a), _ptr(sa), _ld(a), _ld(sa), _ptr(b), _ptr(sb), _ld(b), _ld(sb),
+          int(bmode), _ptr(d), _ld(d), int(dt), M, N, K, _stream(stream))
+
+
+def fp8bs_grouped_gemm(a, sa, b, sb, offsets, d, dt, stream=None):
+    """Per-expert D rows = A rows * B[e]^T; offsets int32 [E+1] on the device."""
+    M_total, K = a.shape
+    E, N, _ = b.shape
+    _call("fp8bs_grouped_gemm", _ptr(a), _ptr(sa), _ld(sa), _ptr(b), _ptr(sb), _ptr(offsets),
+          int(E), M_total, _ptr(d), int(dt), N, K, _stream(stream))
+
+
+# ---------------------------------------------------------------------------
+# allocating helpers (torch tensors on the current device)
+# ---------------------------------------------------------------------------
+
+def quant_act_1x128(x, stream=None):
+    import torch
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    fp8bs_quant_act_1x128(x, q, s, stream)
+    return q, s
+
+
+def quant_w_128x128(w, stream=None):
+    import torch
+    N, K = w.shape
+    q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    s = torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32, device=w.device)
+    fp8bs_quant_w_128x128(w, q, s, stream)
+    return q, s
+
+
+def requant_T_128x1(x, s_in=None, stream=None):
+    """FP8 source when s_in is given (x u8 codes), bf16 source otherwise."""
+    import torch
+    T, C = x.shape
+    Tp = (T + 15) // 16 * 16  # 16-byte aligned output rows
+    q = torch.empty((C, Tp), dtype=torch.uint8, device=x.device)[:, :T]
+    s = torch.empty((C, (T + 127) // 128), dtype=torch.float32, device=x.device)
+    src = SRC_FP8_1x128 if s_in is not None else SRC_BF16
+    fp8bs_requant_T_128x1(src, x, s_in, q, s, stream)
+    return q, s
+
+
+def gemm(a, sa, b, sb, bmode=BSCALE_BLOCK_128x128, out_f32=False, stream=None):
+    import torch
+    M, N = a.shape[0], b.shape[0]
+    d = torch.empty((M, N), dtype=torch.float32 if out_f32 else torch.bfloat16, device=a.device)
+    fp8bs_gemm(a, sa, b, sb, bmode, d, OUT_F32 if out_f32 else OUT_BF16, stream)
+    return d
+
+
+def grouped_gemm(a, sa, b, sb, offsets, out_f32=False, stream=None):
+    import torch
+    M, N = a.shape[0], b.shape[1]
+    d = torch.empty((M, N), dtype=torch.float32 if out_f32 else torch.bfloat16, device=a.device)
+    fp8bs_grouped_gemm(a, sa, b, sb, offsets, d, OUT_F32 if out_f32 else OUT_BF16, stream)
+    return d

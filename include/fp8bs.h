@@ -1,0 +1,165 @@
+/*
+ * fp8bs.h -- C ABI of libfp8bs: fine-grained FP8 quantization and the
+ * block-scaled FP8 GEMM on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the fine-grained FP8 scheme of the DeepSeek-V3 report
+ * excerpts on five web pages, cited as
+ *   [p1] xn--9g3bo1gtkw0l8ubf92bgle.kr board post wr_id=32373
+ *   [p2] why-be.why-be.co.kr board post wr_id=73620
+ *   [p4] bestpmk.kr board post wr_id=299512
+ * with a paragraph number counted on that page.
+ *
+ * Number formats (readings adopted where the pages only say "FP8"):
+ *   - codes are OCP E4M3FN bytes (bias 7, largest finite 448, NaN 0x7F/0xFF,
+ *     no infinities), the byte layout of torch.float8_e4m3fn;
+ *   - every scale is an IEEE binary32 value s = fl32(amax / 448) of the
+ *     max-abs of its tile; a code is the nearest-even E4M3 value of the
+ *     exact quotient x / s, saturated to +-448; an all-zero tile has s = 0
+ *     and signed-zero codes; subnormal scales are kept (no flush to zero);
+ *   - the value a code stands for is dec(code) * s.
+ * Inputs must be finite; NaN or infinite inputs give unspecified codes.
+ *
+ * Conventions for every entry point:
+ *   - All buffers are device memory owned by the caller; the library keeps
+ *     no pointer after the call returns and allocates nothing.
+ *   - Element strides ("ld") are counted in elements of the buffer's type
+ *     and are row strides of row-major matrices.
+ *   - Byte buffers (codes, bf16, fp32 matrices) must be 16-byte aligned and
+ *     their row strides a multiple of 16 bytes; scale buffers must be 4-byte
+ *     aligned and may have any stride at least the row length.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL means the null
+ *     stream) and runs asynchronously; no call synchronizes with the host.
+ *   - Arguments are checked on the host before any HIP call; a failed check
+ *     returns an error and enqueues nothing.  A launch failure returns
+ *     FP8BS_ERR_LAUNCH.  Calls are thread-safe.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP8BS_OK = 0,
+    FP8BS_ERR_INVALID_ARG = 1,      /* null pointer, negative size, bad enum, stride too small */
+    FP8BS_ERR_UNSUPPORTED_SHAPE = 2,/* K (or C) not a multiple of 128 */
+    FP8BS_ERR_MISALIGNED = 3,       /* pointer or row stride breaks the alignment rules */
+    FP8BS_ERR_NO_DEVICE = 4,        /* no HIP device, or the device is not gfx950 */
+    FP8BS_ERR_LAUNCH = 5            /* the kernel launch failed */
+} fp8bs_status;
+
+typedef enum { FP8BS_OUT_BF16 = 0, FP8BS_OUT_F32 = 1 } fp8bs_out_dtype;
+
+typedef enum {
+    FP8BS_BSCALE_BLOCK_128x128 = 0, /* sb[(n/128)*ldsb + k/128]: weight blocks */
+    FP8BS_BSCALE_ROW_1x128 = 1      /* sb[n*ldsb + k/128]: 1x128 tiles along K */
+} fp8bs_bscale;
+
+typedef enum {
+    FP8BS_SRC_FP8_1x128 = 0,        /* E4M3 codes with 1x128 scales */
+    FP8BS_SRC_BF16 = 1              /* plain bf16 */
+} fp8bs_requant_src;
+
+/*
+ * Activation quantization with 1x128 tiles along K.
+ * [p1] para 3: the max-abs is taken online for every 1x128 activation tile,
+ * a scaling factor is derived from it and the tile is quantized to FP8;
+ * [p1] para 2: the scales are per group along the inner dimension K.
+ *   x  bf16 [M][ldx]            input, row m holds K values
+ *   q  u8   [M][ldq]            E4M3 codes
+ *   s  f32  [M][lds]            s[m*lds + g] scales tile (m, g), g < K/128
+ * M >= 0 (0 is a no-op), K > 0 and K % 128 == 0.
+ */
+fp8bs_status fp8bs_quant_act_1x128(const void *x, int64_t M, int64_t K, int64_t ldx,
+                                   uint8_t *q, int64_t ldq, float *s, int64_t lds,
+                                   void *stream);
+
+/*
+ * Weight quantization with 128x128 blocks.
+ * [p1] para 3: the max-abs is taken online for every 128x128 weight block.
+ *   w  bf16 [N][ldw]            input, row n holds K values
+ *   q  u8   [N][ldq]            E4M3 codes
+ *   s  f32  [ceil(N/128)][lds]  s[(n/128)*lds + k/128]
+ * N may be ragged: the last block row takes its max-abs over the rows
+ * present.  N >= 0, K > 0, K % 128 == 0.
+ */
+fp8bs_status fp8bs_quant_w_128x128(const void *w, int64_t N, int64_t K, int64_t ldw,
+                                   uint8_t *q, int64_t ldq, float *s, int64_t lds,
+                                   void *stream);
+
+/*
+ * Backward re-quantization of 1x128 tiles into 128x1 tiles, transposed.
+ * [p1] para 3: in the backward pass the activation tiles are converted
+ * from 1x128 to 128x1; [p1] para 4: activations are cached in FP8 for the
+ * backward pass of the Linear operator.
+ * Reading: v = fl32(dec(q_in[t][c]) * s_in[t][c/128]) (one FP32 multiply);
+ * for src == FP8BS_SRC_BF16, v = x[t][c] and s_in is ignored (may be NULL).
+ * Each run of 128 consecutive tokens t of one channel c is a tile; the
+ * result is written channel-major so that T becomes the contiguous (K)
+ * dimension of a following GEMM.
+ *   in     u8 [T][ld_in] (codes) or bf16 [T][ld_in]
+ *   s_in   f32 [T][lds_in]            s_in[t*lds_in + c/128]
+ *   q_out  u8  [C][ld_out]            q_out[c*ld_out + t]
+ *   s_out  f32 [C][lds_out]           s_out[c*lds_out + t/128], ceil(T/128) per row
+ * T may be ragged (the last token tile takes its max-abs over the tokens
+ * present).  T >= 0, C > 0, C % 128 == 0.
+ */
+fp8bs_status fp8bs_requant_T_128x1(fp8bs_requant_src src, const void *in, const float *s_in,
+                                   int64_t T, int64_t C, int64_t ld_in, int64_t lds_in,
+                                   uint8_t *q_out, int64_t ld_out, float *s_out, int64_t lds_out,
+                                   void *stream);
+
+/*
+ * Block-scaled FP8 GEMM, D = A * B^T, both operands K-contiguous.
+ * [p1] para 2: per-group scales along K are multiplied in as part of
+ * dequantization; [p1] para 3 and [p2] para 1: partial sums are promoted to
+ * FP32 accumulation; [p4] para 4: FP8 inputs, BF16 or FP32 output.
+ * Computed: D[m][n] = sum_g sa[m][g] * sb(n, g) * P_g[m][n] with
+ * P_g = sum over the 128 k of group g of dec(a[m][k]) * dec(b[n][k]);
+ * each P_g is formed in FP32 and added into an FP32 accumulator once per
+ * 128-wide K group, then rounded once to the output type (BF16: nearest-even).
+ *   a   u8  [M][lda]      sa f32 [M][ldsa]       sa[m*ldsa + k/128]
+ *   b   u8  [N][ldb]      sb f32, layout by bmode (see fp8bs_bscale)
+ *   d   bf16 or f32 [M][ldd]
+ * M, N >= 0 (either 0 is a no-op); K > 0, K % 128 == 0.  M and N may be
+ * ragged.
+ */
+fp8bs_status fp8bs_gemm(const uint8_t *a, const float *sa, int64_t lda, int64_t ldsa,
+                        const uint8_t *b, const float *sb, int64_t ldb, int64_t ldsb,
+                        fp8bs_bscale bmode, void *d, int64_t ldd, fp8bs_out_dtype dt,
+                        int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * Grouped block-scaled GEMM for the experts one GPU holds, with ragged
+ * token counts (the per-expert FP8 GEMMs of the MoE layers; [p2] para 2).
+ * Rows offsets[e] .. offsets[e+1]-1 of A are multiplied by expert e:
+ *   D[m][n] = sum_g sa[m][g] * sb[e][n/128][g] * P_g(m, n; b[e])
+ *   a        u8  [M_total][K] (dense rows)   sa f32 [M_total][ldsa]
+ *   b        u8  [E][N][K] (dense)            sb f32 [E][ceil(N/128)][K/128] (dense)
+ *   offsets  i32 [E+1] in DEVICE memory, offsets[0] = 0,
+ *            non-decreasing, offsets[E] = M_total (not checked: a
+ *            violation gives unspecified rows but no out-of-bounds access)
+ *   d        bf16 or f32 [M_total][N] (dense)
+ * M_total sizes the launch only; no host synchronization.
+ * E >= 1, M_total >= 0, N > 0, K > 0, K % 128 == 0.
+ */
+fp8bs_status fp8bs_grouped_gemm(const uint8_t *a, const float *sa, int64_t ldsa,
+                                const uint8_t *b, const float *sb,
+                                const int32_t *offsets, int32_t E, int64_t M_total,
+                                void *d, fp8bs_out_dtype dt, int64_t N, int64_t K,
+                                void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *fp8bs_status_string(fp8bs_status st);
+
+/* Version of the library as major*10000 + minor*100 + patch. */
+int fp8bs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */

@@ -1,0 +1,119 @@
+"""Shared helpers of the GPU parity tests: device transfer, the GEMM
+comparison rules, and cached synthetic inputs with their oracle results.
+
+Comparison rules (from the acceptance bar of the method):
+* quantized codes and scales: bit-exact;
+* FP32 GEMM outputs: relative Frobenius error <= 1e-4 and, per entry,
+  |err| <= 1e-3 * sum_k |a_k||b_k|, against the binary64 oracle;
+* BF16 GEMM outputs: equal to the oracle rounded once to bf16, except
+  isolated one-ulp flips whose oracle value lies within the FP32
+  accumulation error bound of the bf16 rounding midpoint (an FP32 sum can
+  land on either side of it).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from fp8_fine_grained_fp8bs_amd import fp8bs, synth
+
+
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def announce(msg: str):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def bf16_dev(a_u16: np.ndarray) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a_u16).view(np.int16)).view(torch.bfloat16)
+    return t.to(dev())
+
+
+def u8_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+
+
+def f32_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev())
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.contiguous().cpu().numpy()
+
+
+def abs_codes(q: np.ndarray) -> np.ndarray:
+    return (q & 0x7F).astype(np.uint8)
+
+
+def check_quant_equal(name, q_gpu, s_gpu, q_ref, s_ref):
+    assert q_gpu.shape == q_ref.shape and s_gpu.shape == s_ref.shape, name
+    bad_s = np.flatnonzero(s_gpu.view(np.uint32) != s_ref.view(np.uint32))
+    assert bad_s.size == 0, f"{name}: {bad_s.size} scale mismatches, first at {np.unravel_index(bad_s[0], s_ref.shape)}: gpu {s_gpu.flat[bad_s[0]]!r} ref {s_ref.flat[bad_s[0]]!r}"
+    bad_q = np.flatnonzero(q_gpu != q_ref)
+    assert bad_q.size == 0, f"{name}: {bad_q.size} code mismatches, first at {np.unravel_index(bad_q[0], q_ref.shape)}: gpu {q_gpu.flat[bad_q[0]]:#04x} ref {q_ref.flat[bad_q[0]]:#04x}"
+
+
+def check_f32_gemm(name, d_gpu, d_ref, mag):
+    """d_gpu float32, d_ref binary64 oracle, mag = sum |a||b| per entry."""
+    err = d_gpu.astype(np.float64) - d_ref
+    fro = np.linalg.norm(err) / max(np.linalg.norm(d_ref), 1e-300)
+    assert fro <= 1e-4, f"{name}: relative Frobenius {fro:.3e}"
+    ratio = np.abs(err) / np.maximum(mag, 1e-300)
+    worst = float(ratio.max()) if ratio.size else 0.0
+    assert worst <= 1e-3, f"{name}: max |err| / sum|a||b| = {worst:.3e}"
+    return fro, worst
+
+
+def bf16_val(u16: np.ndarray) -> np.ndarray:
+    return synth.bf16_to_f32(u16).astype(np.float64)
+
+
+def check_bf16_gemm(name, d_gpu_u16, d_ref, mag, K):
+    """d_gpu_u16 bf16 bits, d_ref binary64 oracle values."""
+    ref_u16 = oracle.round_to_bf16(d_ref)
+    diff = np.flatnonzero(d_gpu_u16.ravel() != ref_u16.ravel())
+    if diff.size:
+        g = bf16_val(d_gpu_u16.ravel()[diff])
+        r = bf16_val(ref_u16.ravel()[diff])
+        exact = d_ref.ravel()[diff]
+        mid = 0.5 * (g + r)
+        # a flip must come from an FP32 sum landing on the other side of the
+        # rounding midpoint: the exact value lies within 1e-5 * sum|a||b|
+        # of it (FP32 accumulation error is ~1e-7 here, and 1e-5 stays two
+        # orders of magnitude inside the 1e-3 acceptance bound)
+        bound = 1e-5 * mag.ravel()[diff]
+        gu = d_gpu_u16.ravel()[diff].astype(np.int64)
+        ru = ref_u16.ravel()[diff].astype(np.int64)
+        one_ulp = np.abs(gu - ru) == 1
+        near_mid = np.abs(exact - mid) <= bound
+        ok = one_ulp & near_mid
+        assert ok.all(), (f"{name}: {int((~ok).sum())} of {diff.size} bf16 mismatches are not "
+                          f"rounding-boundary flips; first idx {diff[~ok][0]}: gpu {g[~ok][0]!r} "
+                          f"ref {r[~ok][0]!r} exact {exact[~ok][0]!r}")
+        assert diff.size <= max(4, d_ref.size // 1000), f"{name}: {diff.size} flips"
+    return int(diff.size)
+
+
+def gemm_mag(qa, sa, qb, sb, bmode=oracle.BSCALE_BLOCK, mi=None, ni=None):
+    """sum_k |a_k||b_k| per output entry (from the oracle on |codes|, |scales|)."""
+    aa, ab = abs_codes(qa), abs_codes(qb)
+    if mi is None:
+        return oracle.gemm(aa, np.abs(sa), ab, np.abs(sb), bmode)
+    return oracle.gemm_entries(aa, np.abs(sa), ab, np.abs(sb), mi, ni, bmode)
+
+
+def native_loaded():
+    """The HIP library is the code under test: fail loudly if absent."""
+    lib = fp8bs.load()
+    assert lib.fp8bs_version() >= 100
+    return lib

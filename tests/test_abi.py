@@ -1,0 +1,132 @@
+"""CPU tests of the C ABI: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host before any HIP call
+(fake, never dereferenced device addresses are used)."""
+import os
+import re
+
+import pytest
+
+from fp8_fine_grained_fp8bs_amd import fp8bs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bs.h")
+A = 0x100000          # a 16-byte aligned fake device address
+NULL = None
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(fp8bs_[A-Za-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_entry_point():
+    lib = fp8bs.load()
+    names = _declared()
+    assert set(fp8bs.ENTRY_POINTS) <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.fp8bs_version() >= 100
+
+
+def test_status_strings():
+    for code, name in [(0, "FP8BS_OK"), (1, "FP8BS_ERR_INVALID_ARG"), (2, "FP8BS_ERR_UNSUPPORTED_SHAPE"),
+                       (3, "FP8BS_ERR_MISALIGNED"), (4, "FP8BS_ERR_NO_DEVICE"), (5, "FP8BS_ERR_LAUNCH")]:
+        assert fp8bs.status_string(code) == name
+
+
+def quant_act(x=A, M=4, K=256, ldx=256, q=A, ldq=256, s=A, lds=2):
+    return fp8bs.load().fp8bs_quant_act_1x128(x, M, K, ldx, q, ldq, s, lds, NULL)
+
+
+def quant_w(w=A, N=4, K=256, ldw=256, q=A, ldq=256, s=A, lds=2):
+    return fp8bs.load().fp8bs_quant_w_128x128(w, N, K, ldw, q, ldq, s, lds, NULL)
+
+
+def requant(src=0, x=A, s_in=A, T=256, C=128, ld_in=128, lds_in=1, q=A, ld_out=256, s_out=A, lds_out=2):
+    return fp8bs.load().fp8bs_requant_T_128x1(src, x, s_in, T, C, ld_in, lds_in, q, ld_out, s_out, lds_out, NULL)
+
+
+def gemm(a=A, sa=A, lda=256, ldsa=2, b=A, sb=A, ldb=256, ldsb=2, bmode=0, d=A, ldd=64, dt=0,
+         M=8, N=64, K=256):
+    return fp8bs.load().fp8bs_gemm(a, sa, lda, ldsa, b, sb, ldb, ldsb, bmode, d, ldd, dt, M, N, K, NULL)
+
+
+def grouped(a=A, sa=A, ldsa=2, b=A, sb=A, off=A, E=2, M=10, d=A, dt=0, N=128, K=256):
+    return fp8bs.load().fp8bs_grouped_gemm(a, sa, ldsa, b, sb, off, E, M, d, dt, N, K, NULL)
+
+
+@pytest.mark.parametrize("call,expect", [
+    (lambda: quant_act(K=200, ldx=256, ldq=256), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: quant_act(M=-1), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_act(K=0), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_act(x=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_act(q=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_act(s=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_act(ldx=128), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_act(lds=1), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_act(x=A + 8), fp8bs.ERR_MISALIGNED),
+    (lambda: quant_act(q=A + 4), fp8bs.ERR_MISALIGNED),
+    (lambda: quant_act(s=A + 2), fp8bs.ERR_MISALIGNED),
+    (lambda: quant_act(ldx=260), fp8bs.ERR_MISALIGNED),
+    (lambda: quant_act(ldq=264), fp8bs.ERR_MISALIGNED),
+    (lambda: quant_act(M=0, x=NULL, q=NULL, s=NULL), fp8bs.OK),
+    (lambda: quant_w(K=130, ldw=256, ldq=256), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: quant_w(N=-5), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_w(w=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_w(ldq=100), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_w(w=A + 2), fp8bs.ERR_MISALIGNED),
+    (lambda: quant_w(N=0), fp8bs.OK),
+    (lambda: requant(src=7), fp8bs.ERR_INVALID_ARG),
+    (lambda: requant(C=100, ld_in=128), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: requant(T=-1), fp8bs.ERR_INVALID_ARG),
+    (lambda: requant(s_in=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: requant(ld_out=128), fp8bs.ERR_INVALID_ARG),
+    (lambda: requant(lds_out=1), fp8bs.ERR_INVALID_ARG),
+    (lambda: requant(q=A + 1), fp8bs.ERR_MISALIGNED),
+    (lambda: requant(ld_out=264), fp8bs.ERR_MISALIGNED),
+    (lambda: requant(T=0), fp8bs.OK),
+    (lambda: gemm(bmode=2), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm(dt=9), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm(K=192, lda=256, ldb=256), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: gemm(M=-1), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm(a=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm(sb=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm(ldd=32), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm(lda=264), fp8bs.ERR_MISALIGNED),
+    (lambda: gemm(d=A + 4), fp8bs.ERR_MISALIGNED),
+    (lambda: gemm(ldd=68), fp8bs.ERR_MISALIGNED),
+    (lambda: gemm(M=0), fp8bs.OK),
+    (lambda: gemm(N=0), fp8bs.OK),
+    (lambda: grouped(E=0), fp8bs.ERR_INVALID_ARG),
+    (lambda: grouped(off=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: grouped(off=A + 2), fp8bs.ERR_MISALIGNED),
+    (lambda: grouped(K=100), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: grouped(N=0), fp8bs.ERR_INVALID_ARG),
+    (lambda: grouped(N=68), fp8bs.ERR_MISALIGNED),
+    (lambda: grouped(M=0), fp8bs.OK),
+])
+def test_argument_checks_before_any_hip_call(call, expect):
+    assert call() == expect
+
+
+def test_valid_call_without_gpu_reports_no_device():
+    """Host checks pass, then the device query fails cleanly: nothing runs."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert quant_act() == fp8bs.ERR_NO_DEVICE
+    assert gemm() == fp8bs.ERR_NO_DEVICE
+
+
+def test_python_binding_raises_on_error():
+    class Fake:
+        shape = (4, 100)
+        def data_ptr(self):
+            return A
+        def stride(self, i):
+            return (100, 1)[i]
+        def dim(self):
+            return 2
+    with pytest.raises(fp8bs.Fp8bsError) as ei:
+        fp8bs.fp8bs_quant_act_1x128(Fake(), Fake(), Fake(), stream=0)
+    assert ei.value.status == fp8bs.ERR_UNSUPPORTED_SHAPE

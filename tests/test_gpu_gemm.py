@@ -1,0 +1,202 @@
+"""GPU parity of the block-scaled FP8 GEMM and the grouped (MoE) GEMM
+against the binary64 CPU oracle on the same quantized operands."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_fine_grained_fp8bs_amd import fp8bs, synth
+from tests.gpu_common import (announce, check_bf16_gemm, check_f32_gemm, dev, f32_dev,
+                              gemm_mag, host, native_loaded, u8_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _gemm_dev(qa, sa, qb, sb, bmode, out_f32, pads=(0, 0, 0, 0, 0)):
+    """Run fp8bs_gemm on host arrays (optionally with padded row strides)."""
+    M, K = qa.shape
+    N = qb.shape[0]
+    pa, psa, pb, psb, pd = pads
+    a = torch.zeros((M, K + pa), dtype=torch.uint8, device=dev()); a[:, :K] = u8_dev(qa)
+    b = torch.zeros((N, K + pb), dtype=torch.uint8, device=dev()); b[:, :K] = u8_dev(qb)
+    sa_d = torch.zeros((M, sa.shape[1] + psa), dtype=torch.float32, device=dev()); sa_d[:, :sa.shape[1]] = f32_dev(sa)
+    sb_d = torch.zeros((sb.shape[0], sb.shape[1] + psb), dtype=torch.float32, device=dev()); sb_d[:, :sb.shape[1]] = f32_dev(sb)
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    d = torch.full((M, N + pd), 7.0, dtype=dt, device=dev())
+    fp8bs.fp8bs_gemm(a[:, :K], sa_d[:, :sa.shape[1]], b[:, :K], sb_d[:, :sb.shape[1]], bmode,
+                     d[:, :N], fp8bs.OUT_F32 if out_f32 else fp8bs.OUT_BF16)
+    dh = host(d)
+    if pd:
+        tail = dh[:, N:]
+        assert (tail == (7.0 if out_f32 else 0x40E0)).all(), "wrote past the output row"
+    return dh[:, :N]
+
+
+def _full_check(name, qa, sa, qb, sb, bmode=oracle.BSCALE_BLOCK, pads=(0, 0, 0, 0, 0)):
+    ref = oracle.gemm(qa, sa, qb, sb, bmode)
+    mag = gemm_mag(qa, sa, qb, sb, bmode)
+    d32 = _gemm_dev(qa, sa, qb, sb, bmode, True, pads)
+    fro, worst = check_f32_gemm(name + " f32", d32, ref, mag)
+    d16 = _gemm_dev(qa, sa, qb, sb, bmode, False, pads)
+    flips = check_bf16_gemm(name + " bf16", d16, ref, mag, qa.shape[1])
+    announce(f"{name}: f32 rel-fro {fro:.2e} max-err/sum|ab| {worst:.2e}; bf16 flips {flips}")
+
+
+def _sampled_check(name, qa, sa, qb, sb, d_dev, out_f32, bmode=oracle.BSCALE_BLOCK, n=3000, seed=0):
+    M, N = qa.shape[0], qb.shape[0]
+    rng = np.random.default_rng(seed)
+    mi = np.concatenate([rng.integers(0, M, n), [0, M - 1, 0, M - 1], np.full(64, M // 2)])
+    ni = np.concatenate([rng.integers(0, N, n), [0, 0, N - 1, N - 1], np.arange(64) * (N // 64)])
+    ref = oracle.gemm_entries(qa, sa, qb, sb, mi, ni, bmode)
+    mag = gemm_mag(qa, sa, qb, sb, bmode, mi, ni)
+    d = host(d_dev)[mi, ni]
+    if out_f32:
+        fro, worst = check_f32_gemm(name, d, ref, mag)
+        announce(f"{name}: sampled f32 rel-fro {fro:.2e} max-err/sum|ab| {worst:.2e}")
+    else:
+        flips = check_bf16_gemm(name, d, ref, mag, qa.shape[1])
+        announce(f"{name}: sampled bf16 flips {flips} of {mi.size}")
+
+
+def test_gemm_tiny_full():
+    native_loaded()
+    q = synth.tiny()
+    qa, sa = oracle.quant_act_1x128(q["A"])
+    qb, sb = oracle.quant_w_128x128(q["W"])
+    announce("gemm tiny 128x256x512")
+    _full_check("tiny", qa, sa, qb, sb)
+
+
+def test_gemm_probe_full():
+    native_loaded()
+    q = synth.probe()
+    qa, sa = oracle.quant_act_1x128(q["A"])
+    qb, sb = oracle.quant_w_128x128(q["W"])
+    announce("gemm probe 1024x1024x4096")
+    _full_check("probe", qa, sa, qb, sb)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 128), (200, 136, 384), (129, 264, 256), (77, 1000, 640)])
+def test_gemm_ragged_strided(M, N, K):
+    native_loaded()
+    rng = np.random.default_rng(M * 7 + N)
+    q = synth.tiny(M=M, N=N, K=K, seed=M + N)
+    qa, sa = oracle.quant_act_1x128(q["A"])
+    qb, sb = oracle.quant_w_128x128(q["W"])
+    announce(f"gemm ragged {M}x{N}x{K}")
+    _full_check(f"ragged {M}x{N}x{K}", qa, sa, qb, sb, pads=(16, 3, 32, 1, 8))
+    # row mode with per-row scales of B
+    qbr, sbr = oracle.quant_act_1x128(q["W"])
+    _full_check(f"ragged-row {M}x{N}x{K}", qa, sa, qbr, sbr, oracle.BSCALE_ROW, pads=(0, 0, 0, 2, 0))
+
+
+def test_gemm_edge_scales_and_codes():
+    """Zero, subnormal and huge scales; saturated codes; negative zeros."""
+    native_loaded()
+    rng = np.random.default_rng(12)
+    M, N, K = 256, 256, 512
+    qa = rng.integers(0, 256, (M, K)).astype(np.uint8)
+    qb = rng.integers(0, 256, (N, K)).astype(np.uint8)
+    qa[(qa & 0x7F) == 0x7F] = 0x7E
+    qb[(qb & 0x7F) == 0x7F] = 0xFE
+    qa[:8] = 0x7E
+    qb[:4] = 0x80
+    sa = (rng.uniform(0.5, 2, (M, 4)) * 2.0 ** rng.integers(-20, 20, (M, 4))).astype(np.float32)
+    sb = (rng.uniform(0.5, 2, (2, 4)) * 2.0 ** rng.integers(-20, 20, (2, 4))).astype(np.float32)
+    sa[10:20, 1] = 0.0
+    sa[20:30, 2] = np.float32(2.0 ** -140)
+    sb[1, 3] = 0.0
+    announce("gemm edge scales")
+    _full_check("edge", qa, sa, qb, sb)
+
+
+def test_gemm_mlp_up_full_size_sampled():
+    """4096 x 18432 x 7168 (the K = 7168 dense up-projection), the launch
+    configuration the benchmark times; sampled entries vs the oracle."""
+    native_loaded()
+    announce("gemm mlp_up 4096x18432x7168: inputs")
+    d = synth.mlp_up()
+    qa, sa = oracle.quant_act_1x128(d["X"])
+    qb, sb = oracle.quant_w_128x128(d["W"])
+    a, b = u8_dev(qa), u8_dev(qb)
+    sad, sbd = f32_dev(sa), f32_dev(sb)
+    out = fp8bs.gemm(a, sad, b, sbd)
+    _sampled_check("mlp_up bf16", qa, sa, qb, sb, out, False)
+    out32 = fp8bs.gemm(a, sad, b, sbd, out_f32=True)
+    _sampled_check("mlp_up f32", qa, sa, qb, sb, out32, True)
+    h = host(out)
+    assert np.isfinite(synth.bf16_to_f32(h)).all()
+
+
+def test_gemm_wgrad_row_mode_full_size_sampled():
+    """dW [7168][2048] = X^T dY over K = 8192 tokens, operands re-quantized
+    to 128x1 tiles along tokens, FP32 output (row-mode B scales)."""
+    native_loaded()
+    announce("gemm wgrad 7168x2048x8192 row mode")
+    d = synth.wgrad()
+    q1, s1 = oracle.quant_act_1x128(d["X"])
+    qa, sa = oracle.requant_T_128x1_fp8(q1, s1)          # [7168][8192]
+    qb, sb = oracle.requant_T_128x1_bf16(d["dY"])        # [2048][8192]
+    out = fp8bs.gemm(u8_dev(qa), f32_dev(sa), u8_dev(qb), f32_dev(sb), fp8bs.BSCALE_ROW_1x128, out_f32=True)
+    _sampled_check("wgrad f32", qa, sa, qb, sb, out, True, bmode=oracle.BSCALE_ROW)
+
+
+def _grouped_dev(qa, sa, qb, sb, off, out_f32):
+    d = fp8bs.grouped_gemm(u8_dev(qa), f32_dev(sa), u8_dev(qb), f32_dev(sb),
+                           torch.from_numpy(off.astype(np.int32)).to(dev()), out_f32=out_f32)
+    return d
+
+
+def test_grouped_small_full_with_empty_and_tiny_experts():
+    native_loaded()
+    rng = np.random.default_rng(4)
+    counts = np.array([130, 0, 1, 127, 128, 0, 300])
+    off = synth.offsets_from_counts(counts)
+    T, E, N, K = int(off[-1]), len(counts), 256, 384
+    x = synth.tiny(M=T, N=1, K=K, seed=1)["A"]
+    w = synth.tiny(M=1, N=E * N, K=K, seed=2)["W"]
+    qa, sa = oracle.quant_act_1x128(x)
+    qb, sb = oracle.quant_w_128x128(w)
+    qb = qb.reshape(E, N, K); sb = sb.reshape(E, N // 128, K // 128)
+    ref = oracle.grouped_gemm(qa, sa, qb, sb, off)
+    mag = oracle.grouped_gemm(qa & 0x7F, np.abs(sa), qb & 0x7F, np.abs(sb), off)
+    announce(f"grouped small E={E} T={T}")
+    d32 = host(_grouped_dev(qa, sa, qb, sb, off, True))
+    check_f32_gemm("grouped small f32", d32, ref, mag)
+    d16 = host(_grouped_dev(qa, sa, qb, sb, off, False))
+    check_bf16_gemm("grouped small bf16", d16, ref, mag, K)
+
+
+@pytest.mark.parametrize("which", ["up", "down"])
+def test_grouped_moe_full_size_sampled(which):
+    """One GPU's 8 experts, 16384 tokens with Zipf(1.1) counts; gate+up
+    K=7168 -> N=4096 or down K=2048 -> N=7168; sampled entries in every
+    expert, including each expert's first and last row."""
+    native_loaded()
+    announce(f"grouped moe {which}: inputs")
+    parts = ("A_up", "W_up") if which == "up" else ("A_down", "W_down")
+    m = synth.moe(parts=parts)
+    x, w = m[parts[0]], m[parts[1]]
+    E, N, K = w.shape
+    off = m["offsets"]
+    qa, sa = oracle.quant_act_1x128(x)
+    qb, sb = oracle.quant_w_128x128(w.reshape(E * N, K))
+    qb = qb.reshape(E, N, K); sb = sb.reshape(E, N // 128, K // 128)
+    out = _grouped_dev(qa, sa, qb, sb, off, False)
+    rng = np.random.default_rng(1)
+    mi = np.concatenate([rng.integers(0, off[-1], 2000), off[:-1], off[1:] - 1])
+    ni = np.concatenate([rng.integers(0, N, 2000), rng.integers(0, N, 2 * E)])
+    ref = oracle.grouped_gemm_entries(qa, sa, qb, sb, off, mi, ni)
+    mag = oracle.grouped_gemm_entries(qa & 0x7F, np.abs(sa), qb & 0x7F, np.abs(sb), off, mi, ni)
+    flips = check_bf16_gemm(f"grouped {which}", host(out)[mi, ni], ref, mag, K)
+    announce(f"grouped {which}: sampled bf16 flips {flips}")
+
+
+def test_gemm_deterministic():
+    native_loaded()
+    d = synth.mlp_up(T=512, K=1024, N=1024)
+    qa, sa = oracle.quant_act_1x128(d["X"])
+    qb, sb = oracle.quant_w_128x128(d["W"])
+    a = _gemm_dev(qa, sa, qb, sb, oracle.BSCALE_BLOCK, True)
+    b = _gemm_dev(qa, sa, qb, sb, oracle.BSCALE_BLOCK, True)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
