@@ -56,6 +56,7 @@ def _load():
     I32 = ctypes.c_int32
     F32 = ctypes.c_float
     sigs = {
+        "orc_num_threads": (ctypes.c_int, []),
         "orc_e4m3_value": (ctypes.c_double, [ctypes.c_uint8]),
         "orc_e4m3_encode": (ctypes.c_uint8, [ctypes.c_double]),
         "orc_bf16_value": (ctypes.c_double, [ctypes.c_uint16]),
@@ -101,6 +102,11 @@ def _u8(a) -> np.ndarray:
 
 def _f32(a) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def num_threads() -> int:
+    """Threads the oracle's parallel loops use."""
+    return int(_load().orc_num_threads())
 
 
 # --------------------------------------------------------------------------

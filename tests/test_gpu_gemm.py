@@ -6,8 +6,8 @@ import torch
 
 import oracle
 from fp8_fine_grained_fp8bs_amd import fp8bs, synth
-from tests.gpu_common import (announce, check_bf16_gemm, check_f32_gemm, dev, f32_dev,
-                              gemm_mag, host, native_loaded, u8_dev)
+from tests.gpu_common import (announce, bf16_flips, check_bf16_is_rounded_f32, check_f32_gemm,
+                              dev, f32_dev, gemm_mag, host, native_loaded, u8_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,24 +38,33 @@ def _full_check(name, qa, sa, qb, sb, bmode=oracle.BSCALE_BLOCK, pads=(0, 0, 0, 
     d32 = _gemm_dev(qa, sa, qb, sb, bmode, True, pads)
     fro, worst = check_f32_gemm(name + " f32", d32, ref, mag)
     d16 = _gemm_dev(qa, sa, qb, sb, bmode, False, pads)
-    flips = check_bf16_gemm(name + " bf16", d16, ref, mag, qa.shape[1])
-    announce(f"{name}: f32 rel-fro {fro:.2e} max-err/sum|ab| {worst:.2e}; bf16 flips {flips}")
+    check_bf16_is_rounded_f32(name + " bf16", d16, d32)
+    flips = bf16_flips(d16, ref)
+    announce(f"{name}: f32 rel-fro {fro:.2e} max-err/sum|ab| {worst:.2e}; bf16 flips vs rounded oracle {flips}/{ref.size}")
 
 
-def _sampled_check(name, qa, sa, qb, sb, d_dev, out_f32, bmode=oracle.BSCALE_BLOCK, n=3000, seed=0):
-    M, N = qa.shape[0], qb.shape[0]
+def _sample_idx(M, N, n=3000, seed=0):
     rng = np.random.default_rng(seed)
     mi = np.concatenate([rng.integers(0, M, n), [0, M - 1, 0, M - 1], np.full(64, M // 2)])
     ni = np.concatenate([rng.integers(0, N, n), [0, 0, N - 1, N - 1], np.arange(64) * (N // 64)])
+    return mi, ni
+
+
+def _sampled_check(name, qa, sa, qb, sb, d32_dev, d16_dev=None, bmode=oracle.BSCALE_BLOCK):
+    """FP32 result on sampled entries vs the oracle; the BF16 result (if
+    given) on every entry vs the rounded FP32 result."""
+    M, N = qa.shape[0], qb.shape[0]
+    mi, ni = _sample_idx(M, N)
     ref = oracle.gemm_entries(qa, sa, qb, sb, mi, ni, bmode)
     mag = gemm_mag(qa, sa, qb, sb, bmode, mi, ni)
-    d = host(d_dev)[mi, ni]
-    if out_f32:
-        fro, worst = check_f32_gemm(name, d, ref, mag)
-        announce(f"{name}: sampled f32 rel-fro {fro:.2e} max-err/sum|ab| {worst:.2e}")
-    else:
-        flips = check_bf16_gemm(name, d, ref, mag, qa.shape[1])
-        announce(f"{name}: sampled bf16 flips {flips} of {mi.size}")
+    d32 = host(d32_dev)
+    fro, worst = check_f32_gemm(name, d32[mi, ni], ref, mag)
+    msg = f"{name}: sampled f32 rel-fro {fro:.2e} max-err/sum|ab| {worst:.2e}"
+    if d16_dev is not None:
+        d16 = host(d16_dev)
+        check_bf16_is_rounded_f32(name, d16, d32)
+        msg += f"; bf16 == RNE(f32) on all {d16.size}; sampled flips vs rounded oracle {bf16_flips(d16[mi, ni], ref)}"
+    announce(msg)
 
 
 def test_gemm_tiny_full():
@@ -121,11 +130,9 @@ def test_gemm_mlp_up_full_size_sampled():
     a, b = u8_dev(qa), u8_dev(qb)
     sad, sbd = f32_dev(sa), f32_dev(sb)
     out = fp8bs.gemm(a, sad, b, sbd)
-    _sampled_check("mlp_up bf16", qa, sa, qb, sb, out, False)
     out32 = fp8bs.gemm(a, sad, b, sbd, out_f32=True)
-    _sampled_check("mlp_up f32", qa, sa, qb, sb, out32, True)
-    h = host(out)
-    assert np.isfinite(synth.bf16_to_f32(h)).all()
+    _sampled_check("mlp_up", qa, sa, qb, sb, out32, out)
+    assert torch.isfinite(out32).all()
 
 
 def test_gemm_wgrad_row_mode_full_size_sampled():
@@ -138,7 +145,7 @@ def test_gemm_wgrad_row_mode_full_size_sampled():
     qa, sa = oracle.requant_T_128x1_fp8(q1, s1)          # [7168][8192]
     qb, sb = oracle.requant_T_128x1_bf16(d["dY"])        # [2048][8192]
     out = fp8bs.gemm(u8_dev(qa), f32_dev(sa), u8_dev(qb), f32_dev(sb), fp8bs.BSCALE_ROW_1x128, out_f32=True)
-    _sampled_check("wgrad f32", qa, sa, qb, sb, out, True, bmode=oracle.BSCALE_ROW)
+    _sampled_check("wgrad", qa, sa, qb, sb, out, None, bmode=oracle.BSCALE_ROW)
 
 
 def _grouped_dev(qa, sa, qb, sb, off, out_f32):
@@ -164,7 +171,7 @@ def test_grouped_small_full_with_empty_and_tiny_experts():
     d32 = host(_grouped_dev(qa, sa, qb, sb, off, True))
     check_f32_gemm("grouped small f32", d32, ref, mag)
     d16 = host(_grouped_dev(qa, sa, qb, sb, off, False))
-    check_bf16_gemm("grouped small bf16", d16, ref, mag, K)
+    check_bf16_is_rounded_f32("grouped small bf16", d16, d32)
 
 
 @pytest.mark.parametrize("which", ["up", "down"])
@@ -182,14 +189,20 @@ def test_grouped_moe_full_size_sampled(which):
     qa, sa = oracle.quant_act_1x128(x)
     qb, sb = oracle.quant_w_128x128(w.reshape(E * N, K))
     qb = qb.reshape(E, N, K); sb = sb.reshape(E, N // 128, K // 128)
-    out = _grouped_dev(qa, sa, qb, sb, off, False)
+    out16 = _grouped_dev(qa, sa, qb, sb, off, False)
+    out32 = _grouped_dev(qa, sa, qb, sb, off, True)
     rng = np.random.default_rng(1)
-    mi = np.concatenate([rng.integers(0, off[-1], 2000), off[:-1], off[1:] - 1])
-    ni = np.concatenate([rng.integers(0, N, 2000), rng.integers(0, N, 2 * E)])
+    nz = np.flatnonzero(np.diff(off) > 0)
+    mi = np.concatenate([rng.integers(0, off[-1], 2000), off[nz], off[nz + 1] - 1])
+    ni = np.concatenate([rng.integers(0, N, 2000), rng.integers(0, N, 2 * nz.size)])
     ref = oracle.grouped_gemm_entries(qa, sa, qb, sb, off, mi, ni)
     mag = oracle.grouped_gemm_entries(qa & 0x7F, np.abs(sa), qb & 0x7F, np.abs(sb), off, mi, ni)
-    flips = check_bf16_gemm(f"grouped {which}", host(out)[mi, ni], ref, mag, K)
-    announce(f"grouped {which}: sampled bf16 flips {flips}")
+    d32 = host(out32)
+    fro, worst = check_f32_gemm(f"grouped {which} f32", d32[mi, ni], ref, mag)
+    d16 = host(out16)
+    check_bf16_is_rounded_f32(f"grouped {which} bf16", d16, d32)
+    announce(f"grouped {which}: sampled f32 rel-fro {fro:.2e} max-err/sum|ab| {worst:.2e}; "
+             f"bf16 flips vs rounded oracle {bf16_flips(d16[mi, ni], ref)}")
 
 
 def test_gemm_deterministic():
