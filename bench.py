@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Benchmark of the fine-grained FP8 hot path on one MI355X (gfx950).
+
+One step = one forward pass of the K = 7168 dense MLP up-projection:
+  quantize X [4096][7168] in 1x128 tiles, quantize W [18432][7168] in
+  128x128 blocks, and the block-scaled FP8 GEMM Y = X W^T with BF16 output.
+The inputs (seeded synthetic bf16, the heavy-tailed recipe of
+``fp8_fine_grained_fp8bs_amd.synth.mlp_up``) are resident in HBM before the
+timed region starts.  ``value`` is the step's throughput in GEMM TFLOP/s
+(2*M*N*K flop per step divided by the wall time of the step, quantization
+included).  Each kernel is also timed with HIP events on the stream it runs
+on; the GEMM is the dominant kernel and its roofline fraction is reported
+against the MI355X dense FP8 peak.
+
+The other hot-path rows (backward 1x128 -> 128x1 re-quantization, the
+weight-gradient GEMM with row scales, and the grouped MoE GEMMs with their
+quantization) are timed the same way after the step and reported under
+"rows"; they are not part of ``value``.
+
+Prints one JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one
+GPU only.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mlp_up_4096x18432x7168_traffic.txt")
+GEMM_SRC = os.path.join(ROOT, "fp8_fine_grained_fp8bs_amd", "csrc", "gemm.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rows", choices=["all", "none"], default="all",
+                    help="also time the re-quantization, wgrad and grouped rows")
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def bf16_dev(a, dev):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+class KernelTimer:
+    """Per-kernel HIP-event timing on the current stream."""
+
+    def __init__(self):
+        self.events = {}
+
+    def run(self, name, fn):
+        import torch
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.events.setdefault(name, []).append((s, e))
+
+    def mean_ms(self, name):
+        ev = self.events[name]
+        return sum(s.elapsed_time(e) for s, e in ev) / len(ev)
+
+    def reset(self):
+        self.events = {}
+
+
+def gemm_source_hash():
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per GEMM launch from committed counter summaries, only if
+    they were taken on the current GEMM source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("gemm_source_sha256") != gemm_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibrate():
+    import torch
+    dev = torch.device("cuda:0")
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+
+
+def cpu_baseline(x_u16, w_u16, M, N, K):
+    """The oracle as it stands, timed on host cores on a bounded sample of
+    the step, extrapolated linearly to the whole step."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    threads = oracle.num_threads()
+    t0 = time.perf_counter()
+    qa_rows = 256
+    qa, sa = oracle.quant_act_1x128(x_u16[:qa_rows])
+    t_qa = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    qb, sb = oracle.quant_w_128x128(w_u16)
+    t_qw = time.perf_counter() - t0
+    g_rows = min(64, max(8, 2 * threads))
+    t0 = time.perf_counter()
+    oracle.gemm(qa[:g_rows], sa[:g_rows], qb, sb)
+    t_g = time.perf_counter() - t0
+    est = t_qa * (M / qa_rows) + t_qw + t_g * (M / g_rows)
+    value = 2.0 * M * N * K / est / 1e12
+    return {"value": value, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"quant_act of {qa_rows}/{M} rows ({t_qa:.2f} s), quant_w of all {N} rows "
+                       f"({t_qw:.2f} s), GEMM of {g_rows}/{M} rows x {N} x {K} ({t_g:.2f} s); "
+                       f"extrapolated to the full step = {est:.1f} s"),
+            "seconds_measured": t_qa + t_qw + t_g}
+
+
+def time_rows(dev, reps=20, warm=3):
+    """Re-quantization, wgrad GEMM and grouped GEMM rows, at their full sizes."""
+    import numpy as np
+    import torch
+    from fp8_fine_grained_fp8bs_amd import fp8bs, synth
+    rows = {}
+
+    def timed(name, fn):
+        for _ in range(warm):
+            fn()
+        kt = KernelTimer()
+        for _ in range(reps):
+            kt.run(name, fn)
+        torch.cuda.synchronize()
+        return kt.mean_ms(name)
+
+    # backward wgrad: X 8192x7168, dY 8192x2048
+    log("rows: wgrad inputs")
+    w = synth.wgrad()
+    T, C_in = w["X"].shape
+    C_out = w["dY"].shape[1]
+    X = bf16_dev(w["X"], dev)
+    dY = bf16_dev(w["dY"], dev)
+    qx, sx = fp8bs.quant_act_1x128(X)
+    qxt = torch.empty((C_in, T), dtype=torch.uint8, device=dev)
+    sxt = torch.empty((C_in, T // 128), dtype=torch.float32, device=dev)
+    qdt = torch.empty((C_out, T), dtype=torch.uint8, device=dev)
+    sdt = torch.empty((C_out, T // 128), dtype=torch.float32, device=dev)
+    dW = torch.empty((C_in, C_out), dtype=torch.float32, device=dev)
+    ms = timed("requant_fp8", lambda: fp8bs.fp8bs_requant_T_128x1(fp8bs.SRC_FP8_1x128, qx, sx, qxt, sxt))
+    b = T * C_in * (1 + 1) + T * (C_in // 128) * 4 + C_in * (T // 128) * 4
+    rows["requant_T_128x1_fp8"] = {"shape": f"[{T}][{C_in}] -> [{C_in}][{T}]", "us": ms * 1e3,
+                                   "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / HBM_PEAK_GBS,
+                                   "bytes": b}
+    ms = timed("requant_bf16", lambda: fp8bs.fp8bs_requant_T_128x1(fp8bs.SRC_BF16, dY, None, qdt, sdt))
+    b = T * C_out * (2 + 1) + C_out * (T // 128) * 4
+    rows["requant_T_128x1_bf16"] = {"shape": f"[{T}][{C_out}] -> [{C_out}][{T}]", "us": ms * 1e3,
+                                    "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / HBM_PEAK_GBS,
+                                    "bytes": b}
+    ms = timed("wgrad", lambda: fp8bs.fp8bs_gemm(qxt, sxt, qdt, sdt, fp8bs.BSCALE_ROW_1x128, dW, fp8bs.OUT_F32))
+    fl = 2.0 * C_in * C_out * T
+    rows["gemm_wgrad_row_f32"] = {"shape": f"M{C_in} N{C_out} K{T}", "us": ms * 1e3,
+                                  "TFLOP/s": fl / ms / 1e9, "frac_fp8_peak": fl / ms / 1e9 / FP8_PEAK_TFLOPS}
+    del X, dY, qx, sx, qxt, sxt, qdt, sdt, dW, w
+
+    # grouped MoE (8 experts, 16384 tokens, Zipf counts)
+    log("rows: moe inputs")
+    m = synth.moe()
+    off = torch.from_numpy(m["offsets"]).to(dev)
+    Ttok = int(m["offsets"][-1])
+    for tag, an, wn in (("up", "A_up", "W_up"), ("down", "A_down", "W_down")):
+        A = bf16_dev(m[an], dev)
+        E, N, K = m[wn].shape
+        Wt = bf16_dev(m[wn].reshape(E * N, K), dev)
+        qa = torch.empty((Ttok, K), dtype=torch.uint8, device=dev)
+        sa = torch.empty((Ttok, K // 128), dtype=torch.float32, device=dev)
+        qw = torch.empty((E * N, K), dtype=torch.uint8, device=dev)
+        sw = torch.empty((E * N // 128, K // 128), dtype=torch.float32, device=dev)
+        out = torch.empty((Ttok, N), dtype=torch.bfloat16, device=dev)
+        ms = timed(f"qa_{tag}", lambda: fp8bs.fp8bs_quant_act_1x128(A, qa, sa))
+        b = Ttok * K * 3 + Ttok * (K // 128) * 4
+        rows[f"quant_act_moe_{tag}"] = {"shape": f"[{Ttok}][{K}]", "us": ms * 1e3, "GB/s": b / ms / 1e6,
+                                        "frac_hbm": b / ms / 1e6 / HBM_PEAK_GBS, "bytes": b}
+        ms = timed(f"qw_{tag}", lambda: fp8bs.fp8bs_quant_w_128x128(Wt, qw, sw))
+        b = E * N * K * 3 + (E * N // 128) * (K // 128) * 4
+        rows[f"quant_w_moe_{tag}"] = {"shape": f"{E}x[{N}][{K}]", "us": ms * 1e3, "GB/s": b / ms / 1e6,
+                                      "frac_hbm": b / ms / 1e6 / HBM_PEAK_GBS, "bytes": b}
+        qw3, sw3 = qw.view(E, N, K), sw.view(E, N // 128, K // 128)
+        ms = timed(f"grouped_{tag}", lambda: fp8bs.fp8bs_grouped_gemm(qa, sa, qw3, sw3, off, out, fp8bs.OUT_BF16))
+        fl = 2.0 * Ttok * N * K
+        rows[f"grouped_gemm_{tag}"] = {"shape": f"E{E} sumM{Ttok} N{N} K{K}", "us": ms * 1e3,
+                                       "TFLOP/s": fl / ms / 1e9, "frac_fp8_peak": fl / ms / 1e9 / FP8_PEAK_TFLOPS}
+        del A, Wt, qa, sa, qw, sw, out
+    return rows
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from fp8_fine_grained_fp8bs_amd import fp8bs, synth
+
+    if args.copy_calibrate:
+        copy_calibrate()
+        return
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    fp8bs.load()
+
+    M, N, K = 4096, 18432, 7168
+    log("inputs: mlp_up X 4096x7168, W 18432x7168")
+    d = synth.mlp_up(T=M, K=K, N=N)
+    X = bf16_dev(d["X"], dev)
+    W = bf16_dev(d["W"], dev)
+    qx = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sx = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    qw = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    sw = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    kt = KernelTimer()
+
+    def step():
+        kt.run("quant_act", lambda: fp8bs.fp8bs_quant_act_1x128(X, qx, sx))
+        kt.run("quant_w", lambda: fp8bs.fp8bs_quant_w_128x128(W, qw, sw))
+        kt.run("gemm", lambda: fp8bs.fp8bs_gemm(qx, sx, qw, sw, fp8bs.BSCALE_BLOCK_128x128, Y, fp8bs.OUT_BF16))
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kt.reset()
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    assert torch.isfinite(Y.float()).all(), "non-finite GEMM output"
+
+    ms_qa, ms_qw, ms_g = kt.mean_ms("quant_act"), kt.mean_ms("quant_w"), kt.mean_ms("gemm")
+    flop = 2.0 * M * N * K
+    b_qa = M * K * 3 + M * (K // 128) * 4
+    b_qw = N * K * 3 + (N // 128) * (K // 128) * 4
+    gemm_tflops = flop / ms_g / 1e9
+    traffic = read_traffic()
+    kernels = {
+        "quant_act_1x128": {"shape": f"[{M}][{K}]", "us": ms_qa * 1e3, "GB/s": b_qa / ms_qa / 1e6,
+                            "frac_hbm": b_qa / ms_qa / 1e6 / HBM_PEAK_GBS, "bytes": b_qa},
+        "quant_w_128x128": {"shape": f"[{N}][{K}]", "us": ms_qw * 1e3, "GB/s": b_qw / ms_qw / 1e6,
+                            "frac_hbm": b_qw / ms_qw / 1e6 / HBM_PEAK_GBS, "bytes": b_qw},
+        "gemm_bf16_block": {"shape": f"M{M} N{N} K{K}", "us": ms_g * 1e3, "TFLOP/s": gemm_tflops,
+                            "frac_fp8_peak": gemm_tflops / FP8_PEAK_TFLOPS},
+    }
+    result = {
+        "metric": "block-scaled FP8 GEMM TFLOP/s (%FP8 peak) at K=7168; quantize GB/s (%HBM)",
+        "value": flop / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic",
+        "config": {"workload": "dense MLP up-projection forward: quant_act 1x128 of X[4096][7168] + "
+                               "quant_w 128x128 of W[18432][7168] + block-scaled FP8 GEMM Y=X*W^T (BF16 out)",
+                   "M": M, "N": N, "K": K, "inputs": "bf16 X ~N(0,1) with 1% Student-t(3) channels, "
+                                                    "W ~N(0,0.006), seed 0"},
+        "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": gemm_tflops / FP8_PEAK_TFLOPS, "traffic": traffic,
+                     "kernel": "gemm_kernel<bf16 out, block scales>", "flop_per_launch": flop},
+        "kernels": kernels,
+    }
+    if args.rows == "all":
+        result["rows"] = time_rows(dev)
+    if args.cpu_baseline == "on":
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(d["X"], d["W"], M, N, K)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,8 +17,10 @@ namespace {
 // ---------------------------------------------------------------------
 // 1x128 activation tiles.  One wave per row; a 16-lane DPP row per tile,
 // 8 bf16 (16 bytes) per lane, so one wave instruction moves 4 consecutive
-// tiles (1 KiB, fully coalesced).  U tile-quads are loaded before any is
-// processed to keep enough bytes in flight.
+// tiles (1 KiB, fully coalesced).  All U tile-quads of a pass (up to the
+// whole row) are loaded before any is processed, so a wave keeps up to
+// U KiB in flight: enough to cover HBM latency even when the grid is one
+// wave per row and the rows are few.
 // ---------------------------------------------------------------------
 template <int U>
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x, int64_t M,
@@ -35,20 +37,22 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
   float* sr = s + row * lds;
 
   for (int g0 = 0; g0 < G; g0 += 4 * U) {
-    uint4 v[U];
+    u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int g = g0 + 4 * u + grp;
-      if (g < G)
-        v[u] = load16_nt(xr + g * 128);
-      else
-        v[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (g < G) {
+        const uint4 t = load16_nt(xr + g * 128);
+        v[u] = u32x4{t.x, t.y, t.z, t.w};
+      } else {
+        v[u] = u32x4{0u, 0u, 0u, 0u};
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int g = g0 + 4 * u + grp;
-      float f[8] = {bf16_lo(v[u].x), bf16_hi(v[u].x), bf16_lo(v[u].y), bf16_hi(v[u].y),
-                    bf16_lo(v[u].z), bf16_hi(v[u].z), bf16_lo(v[u].w), bf16_hi(v[u].w)};
+      float f[8] = {bf16_lo(v[u][0]), bf16_hi(v[u][0]), bf16_lo(v[u][1]), bf16_hi(v[u][1]),
+                    bf16_lo(v[u][2]), bf16_hi(v[u][2]), bf16_lo(v[u][3]), bf16_hi(v[u][3])};
       float am = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) am = __builtin_fmaxf(am, __builtin_fabsf(f[i]));
@@ -130,10 +134,20 @@ hipError_t launch_quant_act_1x128(const uint16_t* x, int64_t M, int64_t K, int64
   const int64_t blocks = (M + 3) / 4;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks)), block(256);
-  if (G % 8 == 0 && G >= 16)
-    hipLaunchKernelGGL(quant_act_kernel<2>, grid, block, 0, st, x, M, G, ldx, q, ldq, s, lds);
-  else
+  // quads of tiles per pass: the whole row when it has at most 64 tiles
+  const int quads = (G + 3) / 4;
+  if (quads <= 1)
     hipLaunchKernelGGL(quant_act_kernel<1>, grid, block, 0, st, x, M, G, ldx, q, ldq, s, lds);
+  else if (quads <= 2)
+    hipLaunchKernelGGL(quant_act_kernel<2>, grid, block, 0, st, x, M, G, ldx, q, ldq, s, lds);
+  else if (quads <= 4)
+    hipLaunchKernelGGL(quant_act_kernel<4>, grid, block, 0, st, x, M, G, ldx, q, ldq, s, lds);
+  else if (quads <= 8)
+    hipLaunchKernelGGL(quant_act_kernel<8>, grid, block, 0, st, x, M, G, ldx, q, ldq, s, lds);
+  else if (quads <= 14)
+    hipLaunchKernelGGL(quant_act_kernel<14>, grid, block, 0, st, x, M, G, ldx, q, ldq, s, lds);
+  else
+    hipLaunchKernelGGL(quant_act_kernel<16>, grid, block, 0, st, x, M, G, ldx, q, ldq, s, lds);
   return hipGetLastError();
 }
 

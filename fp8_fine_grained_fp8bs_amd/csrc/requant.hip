@@ -8,10 +8,8 @@
 // re-quantized as one tile, and the result is written channel-major so the
 // token dimension becomes the contiguous K of the weight-gradient GEMM.
 //
-// One 256-thread workgroup per 128-token x 128-channel tile; the tile goes
-// through LDS once (an XOR swizzle of 16-byte chunks keeps both the
-// row-wise writes and the 4-token-by-16-channel reads free of bank
-// conflicts), so every input and output byte crosses HBM once.
+// One 256-thread workgroup per tile of 128 tokens; the tile goes through LDS
+// once, so every input and output byte crosses HBM once.
 #include <hip/hip_runtime.h>
 
 #include "fp8bs_device.h"
@@ -20,6 +18,15 @@
 namespace fp8bs {
 namespace {
 
+// Tile: 128 tokens x CW channels (CW = 128 for FP8 codes, 64 for bf16, so
+// a token row of the tile is 128 bytes either way).  Phase 1 copies the
+// tile into LDS with coalesced 16-byte loads.  Phase 2 gives each thread 16
+// consecutive tokens of CPT channels (4 bytes of each token row): the
+// max-abs over a channel's 128 tokens is a reduction over the 8 lanes that
+// share the channel (DPP), each thread derives the scales of only its own
+// CPT channels, and each channel's 16 codes leave as one 16-byte store.
+// Dwords of a row are XOR-swizzled by 8 * ((row / 16) % 4) so that the
+// column reads of phase 2 see at most 2-way bank conflicts.
 template <bool SRC_BF16>
 __global__ __launch_bounds__(256) void requant_kernel(const uint8_t* __restrict__ in,
                                                       const float* __restrict__ s_in, int64_t T,
@@ -27,28 +34,26 @@ __global__ __launch_bounds__(256) void requant_kernel(const uint8_t* __restrict_
                                                       uint8_t* __restrict__ q_out, int64_t ld_out,
                                                       float* __restrict__ s_out, int64_t lds_out) {
   constexpr int ELEM = SRC_BF16 ? 2 : 1;
-  constexpr int ROWB = 128 * ELEM;   // bytes per token row of the tile
-  constexpr int CPR = ROWB / 16;     // 16-byte chunks per row
-  constexpr int RPP = 256 / CPR;     // rows per pass of the workgroup
-  __shared__ __align__(16) uint8_t tile[128 * ROWB];
+  constexpr int CW = SRC_BF16 ? 64 : 128;   // channels per tile
+  constexpr int CPT = SRC_BF16 ? 2 : 4;     // channels per thread
+  __shared__ __align__(16) uint8_t tile[128 * 128];
   __shared__ float srow[128];
 
   const int tid = threadIdx.x;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 128;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * CW;
   const int64_t t0 = static_cast<int64_t>(blockIdx.y) * 128;
 
-  // phase 1: coalesced global -> LDS
+  // phase 1: coalesced global -> LDS, 8 chunks of 16 bytes per token row
   {
-    const int ch = tid % CPR;
+    const int ch = tid & 7;
 #pragma unroll
-    for (int p = 0; p < 128 / RPP; ++p) {
-      const int r = tid / CPR + RPP * p;
+    for (int p = 0; p < 4; ++p) {
+      const int r = (tid >> 3) + 32 * p;
       const int64_t t = t0 + r;
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (t < T)
-        v = load16_nt(in + t * ld_in_bytes + c0 * ELEM + ch * 16);
-      const int phys = ch ^ ((r >> 2) & 7);
-      *reinterpret_cast<uint4*>(tile + r * ROWB + phys * 16) = v;
+      if (t < T) v = load16_nt(in + t * ld_in_bytes + c0 * ELEM + ch * 16);
+      const int phys = ch ^ (2 * ((r >> 4) & 3));
+      *reinterpret_cast<uint4*>(tile + r * 128 + phys * 16) = v;
     }
     if (!SRC_BF16 && tid < 128) {
       const int64_t t = t0 + tid;
@@ -57,61 +62,53 @@ __global__ __launch_bounds__(256) void requant_kernel(const uint8_t* __restrict_
   }
   __syncthreads();
 
-  // phase 2: 4 tokens x 16 channels per thread
-  const int lane = tid & 63;
-  const int tr = lane & 31;                       // tokens 4tr .. 4tr+3
-  const int tc = (tid >> 6) * 2 + (lane >> 5);    // channels 16tc .. 16tc+15
-  float v[4][16];
+  // phase 2
+  const int tg = tid & 7;   // tokens 16 tg .. 16 tg + 15
+  const int cg = tid >> 3;  // dword cg of every row: channels CPT cg .. CPT cg + CPT - 1
+  const int dw = cg ^ (8 * (tg & 3));
+  float v[CPT][16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * tr + i;
-    const int f = (r >> 2) & 7;
+  for (int t = 0; t < 16; ++t) {
+    const int r = 16 * tg + t;
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(tile + r * 128 + dw * 4);
     if (SRC_BF16) {
-      const uint4 a = *reinterpret_cast<const uint4*>(tile + r * ROWB + (((2 * tc) ^ f) * 16));
-      const uint4 b = *reinterpret_cast<const uint4*>(tile + r * ROWB + (((2 * tc + 1) ^ f) * 16));
-      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        v[i][2 * k] = bf16_lo(w[k]);
-        v[i][2 * k + 1] = bf16_hi(w[k]);
-      }
+      v[0][t] = bf16_lo(w);
+      v[1 % CPT][t] = bf16_hi(w);
     } else {
-      const uint4 a = *reinterpret_cast<const uint4*>(tile + r * ROWB + ((tc ^ f) * 16));
       const float s1 = srow[r];
-      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[k]), false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[k]), true);
-        v[i][4 * k + 0] = lo[0] * s1;
-        v[i][4 * k + 1] = lo[1] * s1;
-        v[i][4 * k + 2] = hi[0] * s1;
-        v[i][4 * k + 3] = hi[1] * s1;
-      }
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+      v[0][t] = lo[0] * s1;  // one FP32 multiply: fl32(dec(q) * s1)
+      v[1 % CPT][t] = lo[1] * s1;
+      v[2 % CPT][t] = hi[0] * s1;
+      v[3 % CPT][t] = hi[1] * s1;
     }
   }
 
-  const int64_t tok = t0 + 4 * tr;
-  const bool full = tok + 3 < T;
+  const int64_t tok = t0 + 16 * tg;
+  const bool full = tok + 15 < T;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    float am = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0][j]), __builtin_fabsf(v[1][j])),
-                               __builtin_fmaxf(__builtin_fabsf(v[2][j]), __builtin_fabsf(v[3][j])));
-    am = row16_max(am);
-    am = __int_as_float(max(__float_as_int(am), __shfl_xor(__float_as_int(am), 16)));
-    const TileScale ts = make_tile_scale(am);
-    const float col[4] = {v[0][j], v[1][j], v[2][j], v[3][j]};
-    const uint32_t codes = encode4(col, ts);
-    const int64_t c = c0 + 16 * tc + j;
-    uint8_t* dst = q_out + c * ld_out + tok;
+  for (int c = 0; c < CPT; ++c) {
+    float am = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) am = __builtin_fmaxf(am, __builtin_fabsf(v[c][t]));
+    int x = __float_as_int(am);
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xf, 0xf, false));   // lane ^ 1
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xf, 0xf, false));   // lane ^ 2
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xf, 0xf, false));  // half-row mirror
+    const TileScale ts = make_tile_scale(__int_as_float(x));
+    uint32_t codes[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) codes[k] = encode4(&v[c][4 * k], ts);
+    const int64_t ch = c0 + CPT * cg + c;
+    uint8_t* dst = q_out + ch * ld_out + tok;
     if (full) {
-      *reinterpret_cast<uint32_t*>(dst) = codes;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
     } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (tok + k < T) dst[k] = static_cast<uint8_t>(codes >> (8 * k));
+      for (int k = 0; k < 16; ++k)
+        if (tok + k < T) dst[k] = static_cast<uint8_t>(codes[k / 4] >> (8 * (k % 4)));
     }
-    if (tr == 0) s_out[c * lds_out + blockIdx.y] = ts.s;
+    if (tg == 0) s_out[ch * lds_out + blockIdx.y] = ts.s;
   }
 }
 
@@ -120,7 +117,7 @@ __global__ __launch_bounds__(256) void requant_kernel(const uint8_t* __restrict_
 hipError_t launch_requant_T_128x1(bool src_bf16, const void* in, const float* s_in, int64_t T,
                                   int64_t C, int64_t ld_in, int64_t lds_in, uint8_t* q_out,
                                   int64_t ld_out, float* s_out, int64_t lds_out, hipStream_t st) {
-  const int64_t CB = C / 128;
+  const int64_t CB = src_bf16 ? C / 64 : C / 128;
   const int64_t TB = (T + 127) / 128;
   if (CB > 0x7fffffff || TB > 65535) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(CB), static_cast<unsigned>(TB));
