@@ -27,10 +27,14 @@
 //   per lane per 16-row block.
 // * Workgroup tile 128 (M) x 256 (N), 512 threads = 2 x 4 waves of 64 x 64
 //   (other shapes selectable with FP8BS_GEMM_CFG).
-//   Per K group the A tile (16 KiB) and B tile (32 KiB) go global ->
-//   registers -> LDS; two LDS stages and two register stages put the global
-//   loads two K groups ahead of the MFMAs.  16-byte chunks are XOR-swizzled
-//   with row bits 1..3 so 16 lanes reading 16 rows hit 64 distinct banks.
+//   The A tile (16 KiB), B tile (32 KiB) and scales of a K group are copied
+//   global -> LDS by the load unit itself (global_load_lds_dwordx4: no
+//   staging registers, no LDS write instructions), into three LDS stages:
+//   while group g is multiplied from registers, the fragments of group g+1
+//   are read from LDS and groups g+2 and g+3 are in flight.  16-byte chunks
+//   are XOR-swizzled with row bits 1..3 so 16 lanes reading 16 rows hit 64
+//   distinct banks; the direct loads write that layout by fetching, for LDS
+//   slot (row, chunk p), the global chunk p ^ swizzle(row).
 // * Tiles are handed out XCD-aware: the 8 XCDs each take a contiguous range
 //   of the tile order, and the order walks 4 M-tiles x all N-tiles per
 //   group, so the ~32 workgroups resident on one XCD share A and B panels
@@ -50,18 +54,26 @@ constexpr int GROUP_M = 4;     // M-tiles per group of the tile order
 constexpr int NUM_XCD = 8;
 
 // Workgroup tile BM x BN, WM x WN waves of (BM/WM) x (BN/WN).
-template <int BM_, int BN_, int WM_, int WN_>
+// NSTAGE = 3: fragments of the next K group are read from LDS while the
+// current one is multiplied (two fragment register sets); NSTAGE = 2: each
+// group's fragments are read at the start of its own step (one set, for
+// wave tiles too large to double-buffer).
+template <int BM_, int BN_, int WM_, int WN_, int NSTAGE_ = 3>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-  static constexpr int NT = 64 * WM * WN;         // threads
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NSTAGE = NSTAGE_;
+  static constexpr int NW = WM * WN;              // waves
+  static constexpr int NT = 64 * NW;              // threads
   static constexpr int MB = BM / WM / 16;         // 16-row blocks per wave
   static constexpr int NB = BN / WN / 16;         // 16-column blocks per wave
-  static constexpr int CA = BM * 8 / NT;          // A chunks per thread per K group
-  static constexpr int CB = BN * 8 / NT;          // B chunks per thread per K group
-  static constexpr int RSTEP = NT / 8;            // rows between a thread's chunks
+  static constexpr int A_BYTES = BM * 128;
+  static constexpr int B_BYTES = BN * 128;
+  static constexpr int S_BYTES = NW * 256;        // one 64-float scale slot per wave
+  static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+  static constexpr int DPW = (BM + BN) / 8 / NW;  // 1 KiB tile copies per wave per K group
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
-  static_assert(CA >= 1 && CB >= 1 && BM * 8 % NT == 0 && BN * 8 % NT == 0, "staging");
-  static_assert(NT >= BM + BN, "one scale slot per thread");
+  static_assert((BM + BN) % (8 * NW) == 0, "tile copies must split evenly over the waves");
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && BM / 64 + BN / 64 <= NW, "one scale copy per wave");
+  static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS stages");
 };
 
 #ifndef FP8BS_GEMM_CFG
@@ -74,8 +86,10 @@ using MainCfg = Cfg<128, 128, 2, 2>;
 #elif FP8BS_GEMM_CFG == 2
 using MainCfg = Cfg<128, 256, 2, 4>;
 #else
-using MainCfg = Cfg<256, 256, 4, 4>;
+using MainCfg = Cfg<256, 256, 2, 4, 2>;
 #endif
+// Row-scale mode holds 16 more scales per fragment set: narrower wave tiles.
+using RowCfg = Cfg<128, 128, 2, 4>;
 
 struct GemmArgs {
   const uint8_t* a;
@@ -115,49 +129,107 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   nt = rr / gm;
 }
 
-// Per-thread staging registers of one K group.
+// Direct global -> LDS copies.  global_load_lds_dword{,x4} writes lane l's
+// 4 (16) bytes at M0 + 4 l (16 l); M0 is saved and restored around the copy
+// so no compiler-owned use of M0 is disturbed.  The compiler does not see
+// these as LDS writes: completion is waited for explicitly with vmcnt
+// before the barrier that publishes a stage.
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds_addr), "v"(src) : "memory");
+}
+__device__ __forceinline__ void copy4_to_lds(const void* src, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds_addr), "v"(src) : "memory");
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int WAIT_LGKM0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Fragments (and their scales) of one K group for one wave.
 template <class C>
-struct Stage {
-  u32x4 a[C::CA];
-  u32x4 b[C::CB];
-  float s;
+struct Frag {
+  v8i fb[C::NB];     // B tile rows (MFMA A operand)
+  v8i fa[C::MB];     // A tile rows (MFMA B operand)
+  float sam[C::MB];  // A scale of this lane's row in each 16-row block
+  float sbn[C::NB][4];  // row mode: B scales of this lane's 4 columns per block
+  float sbv;            // block mode: the wave's B block scale
 };
 
-template <class C>
-__device__ __forceinline__ void fetch(Stage<C>& st, const uint8_t* const (&ga)[C::CA],
-                                      const uint8_t* const (&gb)[C::CB], const float* gs, int64_t g) {
-#pragma unroll
-  for (int i = 0; i < C::CA; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(ga[i] + g * 128);
-#pragma unroll
-  for (int i = 0; i < C::CB; ++i) st.b[i] = *reinterpret_cast<const u32x4*>(gb[i] + g * 128);
-  st.s = gs[g];
-}
-
-// Registers -> one LDS stage.  Every thread stores its scale: slots
-// 0..BM-1 are the A scales of the tile rows, BM.. the B scales (one per
-// tile row in row mode, one per 128-wide column block in block mode), the
-// rest are never read.
-template <class C>
-__device__ __forceinline__ void stash(const Stage<C>& st, uint8_t* la, uint8_t* lb, float* ls,
-                                      int tid, int ld_r, int ld_ch) {
-#pragma unroll
-  for (int i = 0; i < C::CA; ++i) *reinterpret_cast<u32x4*>(la + swz(ld_r + C::RSTEP * i, ld_ch)) = st.a[i];
-#pragma unroll
-  for (int i = 0; i < C::CB; ++i) *reinterpret_cast<u32x4*>(lb + swz(ld_r + C::RSTEP * i, ld_ch)) = st.b[i];
-  ls[tid] = st.s;
-}
-
-// One K group on one LDS stage: MB x NB MFMAs and their promotions per wave.
 template <class C, bool BROW>
-__device__ __forceinline__ void compute(v4f (&acc)[C::MB][C::NB], const uint8_t* la, const uint8_t* lb,
-                                        const float* ls, float sbv, int wm, int wn, int lane) {
+__device__ __forceinline__ void load_frag(Frag<C>& f, const uint8_t* stage, int wm, int wn, int lane) {
   constexpr int TM = C::MB * 16, TN = C::NB * 16;
-  const float* lsa = ls;
-  const float* lsb = ls + C::BM;
-  // block mode: this wave's B block scale (staged in slot BM + block)
-  if (!BROW) sbv = lsb[(wn * TN) / 128];
+  const uint8_t* la = stage;
+  const uint8_t* lb = stage + C::A_BYTES;
+  const float* ls = reinterpret_cast<const float*>(stage + C::A_BYTES + C::B_BYTES);
   const int fr = lane & 15;
   const int kc = lane >> 4;  // k chunks kc and kc + 4 (any permutation shared by A and B is valid)
+#pragma unroll
+  for (int j = 0; j < C::NB; ++j) {
+    const int r = wn * TN + j * 16 + fr;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(lb + swz(r, kc));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(lb + swz(r, kc + 4));
+    f.fb[j] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+#pragma unroll
+  for (int i = 0; i < C::MB; ++i) {
+    const int r = wm * TM + i * 16 + fr;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(la + swz(r, kc));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(la + swz(r, kc + 4));
+    f.fa[i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    f.sam[i] = ls[r];
+  }
+  if (BROW) {
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j) {
+      const float4 v = *reinterpret_cast<const float4*>(ls + C::BM + wn * TN + j * 16 + 4 * kc);
+      f.sbn[j][0] = v.x; f.sbn[j][1] = v.y; f.sbn[j][2] = v.z; f.sbn[j][3] = v.w;
+    }
+  } else {
+    f.sbv = ls[C::BM + (wn * TN) / 128];
+  }
+}
+
+// One K group from registers: MB x NB MFMAs and their promotions per wave.
+template <class C, bool BROW>
+__device__ __forceinline__ void compute(v4f (&acc)[C::MB][C::NB], const Frag<C>& f) {
+  // Keep the matrix core fed: raise this wave's issue priority for the MFMA
+  // block and let the scheduler interleave the other work with the MFMAs.
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_iglp_opt(0);
+#pragma unroll
+  for (int i = 0; i < C::MB; ++i) {
+    const float sc = f.sam[i] * f.sbv;
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j) {
+      const v4f part = mfma_16x16x128_fp8(f.fb[j], f.fa[i]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float s = BROW ? f.sam[i] * f.sbn[j][q] : sc;
+        acc[i][j][q] = __builtin_fmaf(part[q], s, acc[i][j][q]);
+      }
+    }
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// One K group straight from an LDS stage (two-stage pipeline): the B-tile
+// fragments are read once, the A-tile fragments block by block with the
+// next block's read issued before the current block's MFMAs.
+template <class C, bool BROW>
+__device__ __forceinline__ void compute_lds(v4f (&acc)[C::MB][C::NB], const uint8_t* stage, int wm,
+                                            int wn, int lane) {
+  constexpr int TM = C::MB * 16, TN = C::NB * 16;
+  const uint8_t* la = stage;
+  const uint8_t* lb = stage + C::A_BYTES;
+  const float* ls = reinterpret_cast<const float*>(stage + C::A_BYTES + C::B_BYTES);
+  const int fr = lane & 15;
+  const int kc = lane >> 4;
   v8i fb[C::NB];
 #pragma unroll
   for (int j = 0; j < C::NB; ++j) {
@@ -167,36 +239,32 @@ __device__ __forceinline__ void compute(v4f (&acc)[C::MB][C::NB], const uint8_t*
     fb[j] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   }
   float sbn[C::NB][4];
+  float sbv = 0.0f;
   if (BROW) {
 #pragma unroll
     for (int j = 0; j < C::NB; ++j) {
-      const float4 v = *reinterpret_cast<const float4*>(lsb + wn * TN + j * 16 + 4 * kc);
+      const float4 v = *reinterpret_cast<const float4*>(ls + C::BM + wn * TN + j * 16 + 4 * kc);
       sbn[j][0] = v.x; sbn[j][1] = v.y; sbn[j][2] = v.z; sbn[j][3] = v.w;
     }
+  } else {
+    sbv = ls[C::BM + (wn * TN) / 128];
   }
-  v8i fa[C::MB];
-  float sam[C::MB];
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
   for (int i = 0; i < C::MB; ++i) {
     const int r = wm * TM + i * 16 + fr;
     const u32x4 lo = *reinterpret_cast<const u32x4*>(la + swz(r, kc));
     const u32x4 hi = *reinterpret_cast<const u32x4*>(la + swz(r, kc + 4));
-    fa[i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    sam[i] = lsa[r];
-  }
-  // Keep the matrix core fed: raise this wave's issue priority for the MFMA
-  // block and ask the scheduler to interleave the LDS reads with the MFMAs.
-  __builtin_amdgcn_s_setprio(1);
-  __builtin_amdgcn_iglp_opt(0);
-#pragma unroll
-  for (int i = 0; i < C::MB; ++i) {
-    const float sc = sam[i] * sbv;
+    const v8i fa = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    const float sam = ls[r];
+    const float sc = sam * sbv;
 #pragma unroll
     for (int j = 0; j < C::NB; ++j) {
-      const v4f part = mfma_16x16x128_fp8(fb[j], fa[i]);
+      const v4f part = mfma_16x16x128_fp8(fb[j], fa);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float s = BROW ? sam[i] * sbn[j][q] : sc;
+        const float s = BROW ? sam * sbn[j][q] : sc;
         acc[i][j][q] = __builtin_fmaf(part[q], s, acc[i][j][q]);
       }
     }
@@ -207,13 +275,11 @@ __device__ __forceinline__ void compute(v4f (&acc)[C::MB][C::NB], const uint8_t*
 template <class C, bool OUT_F32, bool BROW, bool GROUPED>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   constexpr int BM = C::BM, BN = C::BN;
-  __shared__ __align__(16) uint8_t lds_a[2][BM * 128];
-  __shared__ __align__(16) uint8_t lds_b[2][BN * 128];
-  __shared__ __align__(16) float lds_s[2][C::NT];
+  __shared__ __align__(16) uint8_t lds[C::NSTAGE * C::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int64_t G = p.K / 128;
 
@@ -247,48 +313,67 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     m0 = static_cast<int64_t>(vm) * BM;
     m_end = p.M;
   }
-
-  // ---- staging layout: thread t moves 16-byte chunk (t & 7) of rows
-  //      (t >> 3) + RSTEP i of the A tile (i < CA) and of the B tile (i < CB)
-  const int ld_ch = tid & 7;
-  const int ld_r = tid >> 3;
-  const uint8_t* ga[C::CA];
-  const uint8_t* gb[C::CB];
-#pragma unroll
-  for (int i = 0; i < C::CA; ++i) {
-    int64_t r = m0 + ld_r + C::RSTEP * i;
-    r = r < m_end ? r : m_end - 1;
-    ga[i] = p.a + r * p.lda + ld_ch * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < C::CB; ++i) {
-    int64_t r = n0 + ld_r + C::RSTEP * i;
-    r = r < p.N ? r : p.N - 1;
-    gb[i] = bmat + r * p.ldb + ld_ch * 16;
-  }
-  // scales: threads t < BM fetch sa of row m0 + t; threads BM .. BM+BN-1
-  // fetch sb of row n0 + t - BM in row mode; every other thread re-reads row m0's
-  // sa (a valid address, value unused) so the loop has no branch
-  const float* gs;
-  if (tid < BM) {
-    int64_t r = m0 + tid;
-    r = r < m_end ? r : m_end - 1;
-    gs = p.sa + r * p.ldsa;
-  } else if (BROW && tid < BM + BN) {
-    int64_t r = n0 + tid - BM;
-    r = r < p.N ? r : p.N - 1;
-    gs = sbmat + r * p.ldsb;
-  } else if (!BROW && tid < BM + BN / 128) {
-    // block mode: the B block scales of this tile's 128-wide column blocks
-    int64_t blk = n0 / 128 + (tid - BM);
-    const int64_t last_blk = (p.N - 1) / 128;
-    blk = blk < last_blk ? blk : last_blk;
-    gs = sbmat + blk * p.ldsb;
-  } else {
-    gs = p.sa + m0 * p.ldsa;
-  }
   // block mode: a wave's columns lie inside one 128-wide block of B
   static_assert(BROW || (128 % (C::NB * 16) == 0), "wave columns must not straddle a B block");
+
+  // ---- copy plan: the tile rows of a K group are DPW 1 KiB copies per
+  //      wave (8 rows each, A rows first, then B rows); lane l fetches the
+  //      global chunk (l & 7) ^ swizzle(row) of row l / 8 of its copy
+  const uint8_t* src[C::DPW];
+  uint32_t dst_off[C::DPW];
+#pragma unroll
+  for (int q = 0; q < C::DPW; ++q) {
+    const int I = wave * C::DPW + q;               // copy index within the K group
+    const bool isA = I < BM / 8;
+    const int r = (isA ? I : I - BM / 8) * 8 + (lane >> 3);  // row inside its tile
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    int64_t grow;
+    if (isA) {
+      grow = m0 + r;
+      grow = grow < m_end ? grow : m_end - 1;
+      src[q] = p.a + grow * p.lda + c * 16;
+    } else {
+      grow = n0 + r;
+      grow = grow < p.N ? grow : p.N - 1;
+      src[q] = bmat + grow * p.ldb + c * 16;
+    }
+    dst_off[q] = isA ? I * 1024 : C::A_BYTES + (I - BM / 8) * 1024;
+  }
+  // one scale copy per wave (64 floats into the wave's slot): A scales of
+  // 64 tile rows, then B scales (row mode: 64 rows; block mode: the column
+  // blocks), the remaining waves re-read a valid A-scale row (unused)
+  const float* ssrc;
+  {
+    const int SA = BM / 64, SB = BROW ? BN / 64 : 1;
+    if (wave < SA) {
+      int64_t r = m0 + wave * 64 + lane;
+      r = r < m_end ? r : m_end - 1;
+      ssrc = p.sa + r * p.ldsa;
+    } else if (wave < SA + SB) {
+      if (BROW) {
+        int64_t r = n0 + (wave - SA) * 64 + lane;
+        r = r < p.N ? r : p.N - 1;
+        ssrc = sbmat + r * p.ldsb;
+      } else {
+        int64_t blk = n0 / 128 + lane;
+        const int64_t last_blk = (p.N - 1) / 128;
+        blk = blk < last_blk ? blk : last_blk;
+        ssrc = sbmat + blk * p.ldsb;
+      }
+    } else {
+      ssrc = p.sa + m0 * p.ldsa;
+    }
+  }
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&lds[0]));
+  const uint32_t s_off = C::A_BYTES + C::B_BYTES + wave * 256;
+  constexpr int COPIES = C::DPW + 1;  // vector-memory ops per wave per K group
+
+  auto issue = [&](int64_t g, int stage) {
+    const uint32_t base = lds_base + stage * C::STAGE;
+#pragma unroll
+    for (int q = 0; q < C::DPW; ++q) copy16_to_lds(src[q] + g * 128, base + dst_off[q]);
+    copy4_to_lds(ssrc + g, base + s_off);
+  };
 
   v4f acc[C::MB][C::NB];
 #pragma unroll
@@ -296,32 +381,67 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < C::NB; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  Stage<C> s0, s1;
-  fetch(s0, ga, gb, gs, 0);
-  fetch(s1, ga, gb, gs, G > 1 ? 1 : 0);
-  stash(s0, lds_a[0], lds_b[0], lds_s[0], tid, ld_r, ld_ch);
-  __syncthreads();
-
-  // Pair of iterations (g, g + 1): set s0 is refilled with group g + 2 while
-  // stage 0 (group g) is multiplied, then set s1 (group g + 1) goes to stage
-  // 1; symmetrically for g + 1.  The loop body has no branch: prefetch
-  // indices past the end are clamped to the last group (re-read, never
-  // multiplied), so the compiler can keep two groups of loads in flight and
-  // interleave the promotion FMAs with the MFMAs.
   const int64_t last = G - 1;
-  int64_t g = 0;
-  for (; g + 2 <= G; g += 2) {
-    fetch(s0, ga, gb, gs, g + 2 < last ? g + 2 : last);
-    compute<C, BROW>(acc, lds_a[0], lds_b[0], lds_s[0], 0.0f, wm, wn, lane);
-    stash(s1, lds_a[1], lds_b[1], lds_s[1], tid, ld_r, ld_ch);
-    __syncthreads();
-    fetch(s1, ga, gb, gs, g + 3 < last ? g + 3 : last);
-    compute<C, BROW>(acc, lds_a[1], lds_b[1], lds_s[1], 0.0f, wm, wn, lane);
-    stash(s0, lds_a[0], lds_b[0], lds_s[0], tid, ld_r, ld_ch);
-    __syncthreads();
+  auto clampg = [&](int64_t x) { return x < last ? x : last; };
+  if constexpr (C::NSTAGE == 3) {
+    // Pipeline over three stages, stage(x) = x % 3.  Before iteration g:
+    // fragments of group g are in registers (cur), stage(g + 1) holds group
+    // g + 1 and is visible, the copy of group g + 2 into stage(g + 2) is in
+    // flight.  Iteration g reads the fragments of g + 1, starts the copy of
+    // g + 3 into stage(g) (whose reads finished before the last barrier),
+    // multiplies g, then waits for the copy of g + 2 and for its own LDS
+    // reads before the barrier.  Copies and reads past the last group are
+    // clamped to the last group: they move valid data that is never used.
+    issue(0, 0);
+    issue(clampg(1), 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    block_barrier();
+    Frag<C> f0, f1;
+    load_frag<C, BROW>(f0, lds, wm, wn, lane);
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+    issue(clampg(2), 2);
+    block_barrier();
+
+    int64_t g = 0;
+    int st1 = 1;  // stage(g + 1)
+    for (; g + 2 <= G; g += 2) {
+      // iteration g: cur = f0, next = f1
+      load_frag<C, BROW>(f1, lds + st1 * C::STAGE, wm, wn, lane);
+      issue(clampg(g + 3), st1 == 0 ? 2 : st1 - 1);
+      compute<C, BROW>(acc, f0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(COPIES));
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+      block_barrier();
+      st1 = st1 == 2 ? 0 : st1 + 1;
+      // iteration g + 1: cur = f1, next = f0
+      load_frag<C, BROW>(f0, lds + st1 * C::STAGE, wm, wn, lane);
+      issue(clampg(g + 4), st1 == 0 ? 2 : st1 - 1);
+      compute<C, BROW>(acc, f1);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(COPIES));
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+      block_barrier();
+      st1 = st1 == 2 ? 0 : st1 + 1;
+    }
+    if (g < G)  // odd G: the last group's fragments are in f0
+      compute<C, BROW>(acc, f0);
+  } else {
+    // Two stages, stage(x) = x % 2.  Iteration g starts the copy of g + 1
+    // into the other stage (read during iteration g - 1, finished before
+    // the last barrier), multiplies g straight from LDS, then waits for the
+    // copy and its own reads before the barrier.
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    block_barrier();
+    for (int64_t g = 0; g < G; ++g) {
+      const int st = static_cast<int>(g & 1);
+      issue(clampg(g + 1), st ^ 1);
+      compute_lds<C, BROW>(acc, lds + st * C::STAGE, wm, wn, lane);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+      block_barrier();
+    }
   }
-  if (g < G)  // odd G: stage 0 holds the last group
-    compute<C, BROW>(acc, lds_a[0], lds_b[0], lds_s[0], 0.0f, wm, wn, lane);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // drain the clamped copies before exit
 
   // ---- epilogue: lane holds columns n .. n+3 of row m per 16x16 block ----
   const int fr = lane & 15;
@@ -357,17 +477,15 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   }
 }
 
-template <class C, bool GROUPED>
-hipError_t dispatch(const GemmArgs& args, bool brow, bool out_f32, hipStream_t st) {
-  const int64_t total = static_cast<int64_t>(args.tiles_m) * args.tiles_n;
-  const dim3 grid(static_cast<unsigned>(total)), block(C::NT);
-  if (out_f32) {
-    if (brow) hipLaunchKernelGGL((gemm_kernel<C, true, true, GROUPED>), grid, block, 0, st, args);
-    else hipLaunchKernelGGL((gemm_kernel<C, true, false, GROUPED>), grid, block, 0, st, args);
-  } else {
-    if (brow) hipLaunchKernelGGL((gemm_kernel<C, false, true, GROUPED>), grid, block, 0, st, args);
-    else hipLaunchKernelGGL((gemm_kernel<C, false, false, GROUPED>), grid, block, 0, st, args);
-  }
+template <class C, bool BROW, bool GROUPED>
+hipError_t dispatch(GemmArgs args, int64_t tiles_m_extra, bool out_f32, hipStream_t st) {
+  const int64_t tm = (args.M + C::BM - 1) / C::BM + tiles_m_extra, tn = (args.N + C::BN - 1) / C::BN;
+  if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
+  args.tiles_m = static_cast<int32_t>(tm);
+  args.tiles_n = static_cast<int32_t>(tn);
+  const dim3 grid(static_cast<unsigned>(tm * tn)), block(C::NT);
+  if (out_f32) hipLaunchKernelGGL((gemm_kernel<C, true, BROW, GROUPED>), grid, block, 0, st, args);
+  else hipLaunchKernelGGL((gemm_kernel<C, false, BROW, GROUPED>), grid, block, 0, st, args);
   return hipGetLastError();
 }
 
@@ -381,12 +499,8 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t l
   args.a = a; args.sa = sa; args.b = b; args.sb = sb; args.d = d; args.offsets = nullptr;
   args.lda = lda; args.ldsa = ldsa; args.ldb = ldb; args.ldsb = ldsb; args.ldd = ldd;
   args.M = M; args.N = N; args.K = K; args.E = 0;
-  using C = MainCfg;
-  const int64_t tm = (M + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
-  if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
-  args.tiles_m = static_cast<int32_t>(tm);
-  args.tiles_n = static_cast<int32_t>(tn);
-  return dispatch<C, false>(args, bscale_row, out_f32, st);
+  if (bscale_row) return dispatch<RowCfg, true, false>(args, 0, out_f32, st);
+  return dispatch<MainCfg, false, false>(args, 0, out_f32, st);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, int64_t ldsa,
@@ -399,12 +513,7 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, int64_t ldsa,
   args.M = M_total; args.N = N; args.K = K; args.E = E;
   // upper bound of the per-expert M-tile count: each expert adds at most one
   // partial tile
-  using C = MainCfg;
-  const int64_t tm = (M_total + C::BM - 1) / C::BM + E, tn = (N + C::BN - 1) / C::BN;
-  if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
-  args.tiles_m = static_cast<int32_t>(tm);
-  args.tiles_n = static_cast<int32_t>(tn);
-  return dispatch<C, true>(args, false, out_f32, st);
+  return dispatch<MainCfg, false, true>(args, E, out_f32, st);
 }
 
 }  // namespace fp8bs
