@@ -17,8 +17,8 @@ weight-gradient GEMM with row scales, and the grouped MoE GEMMs with their
 quantization) are timed the same way after the step and reported under
 "rows"; they are not part of ``value``.
 
-Prints one JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one
-GPU only.
+Prints one JSON line.  ``--gpus N`` with N > 1 exits: the path is
+single-GPU (no collectives).
 """
 from __future__ import annotations
 
@@ -226,8 +226,8 @@ def time_rows(dev, reps=20, warm=3):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); this build has no "
-              "multi-GPU path.", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); the library has "
+              "no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
