@@ -17,6 +17,11 @@ constexpr int kMaxDevices = 64;
 // 0 = unknown, 1 = gfx950, 2 = other architecture
 std::atomic<int> g_dev_state[kMaxDevices];
 
+// GEMM stride limits: a 256-row tile of codes or scales must span less than
+// 4 GiB, so that 32-bit offsets from its first row reach every element.
+constexpr int64_t kMaxCodeStride = int64_t(1) << 24;   // bytes per code row
+constexpr int64_t kMaxScaleStride = int64_t(1) << 22;  // floats per scale row
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 fp8bs_status check_device() {
@@ -147,6 +152,10 @@ fp8bs_status fp8bs_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t 
   FP8BS_TRY(check_scales(sa, K / 128, ldsa));
   FP8BS_TRY(check_scales(sb, K / 128, ldsb));
   FP8BS_TRY(check_matrix(d, N, ldd, dt == FP8BS_OUT_F32 ? 4 : 2));
+  // tiles are addressed with 32-bit offsets from their first row
+  if (lda >= kMaxCodeStride || ldb >= kMaxCodeStride || ldsa >= kMaxScaleStride ||
+      ldsb >= kMaxScaleStride)
+    return FP8BS_ERR_UNSUPPORTED_SHAPE;
   FP8BS_TRY(check_device());
   return launched(fp8bs::launch_gemm(a, sa, lda, ldsa, b, sb, ldb, ldsb,
                                      bmode == FP8BS_BSCALE_ROW_1x128, d, ldd, dt == FP8BS_OUT_F32,
@@ -167,6 +176,7 @@ fp8bs_status fp8bs_grouped_gemm(const uint8_t* a, const float* sa, int64_t ldsa,
   FP8BS_TRY(check_matrix(a, K, K, 1));
   FP8BS_TRY(check_scales(sa, K / 128, ldsa));
   FP8BS_TRY(check_matrix(d, N, N, dt == FP8BS_OUT_F32 ? 4 : 2));
+  if (K >= kMaxCodeStride || ldsa >= kMaxScaleStride) return FP8BS_ERR_UNSUPPORTED_SHAPE;
   FP8BS_TRY(check_device());
   return launched(fp8bs::launch_grouped_gemm(a, sa, ldsa, b, sb, offsets, E, M_total, d,
                                              dt == FP8BS_OUT_F32, N, K,

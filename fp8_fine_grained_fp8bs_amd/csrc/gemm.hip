@@ -27,14 +27,20 @@
 //   per lane per 16-row block.
 // * Workgroup tile 128 (M) x 256 (N), 512 threads = 2 x 4 waves of 64 x 64
 //   (other shapes selectable with FP8BS_GEMM_CFG).
-//   The A tile (16 KiB), B tile (32 KiB) and scales of a K group are copied
-//   global -> LDS by the load unit itself (global_load_lds_dwordx4: no
+//   The A tile (16 KiB) and B tile (32 KiB) of a K group are copied
+//   global -> LDS by the load unit itself (buffer_load_dwordx4 ... lds: no
 //   staging registers, no LDS write instructions), into three LDS stages:
 //   while group g is multiplied from registers, the fragments of group g+1
 //   are read from LDS and groups g+2 and g+3 are in flight.  16-byte chunks
 //   are XOR-swizzled with row bits 1..3 so 16 lanes reading 16 rows hit 64
 //   distinct banks; the direct loads write that layout by fetching, for LDS
-//   slot (row, chunk p), the global chunk p ^ swizzle(row).
+//   slot (row, chunk p), the global chunk p ^ swizzle(row).  Buffer
+//   descriptors bound each copy to the tile's valid rows (rows past the
+//   end read as zeros), so every per-copy offset is uniform.
+// * The FP32 scales travel in blocks of 4 K groups through a 3-slot LDS
+//   ring, one quarter block per K group: each lane fetches 4 consecutive
+//   groups of one row, so a row's scales cost one cache line per 4 groups
+//   instead of one per group.
 // * Tiles are handed out XCD-aware: the 8 XCDs each take a contiguous range
 //   of the tile order, and the order walks 4 M-tiles x all N-tiles per
 //   group, so the ~32 workgroups resident on one XCD share A and B panels
@@ -52,6 +58,8 @@ typedef __attribute__((ext_vector_type(4))) float v4f;
 
 constexpr int GROUP_M = 4;     // M-tiles per group of the tile order
 constexpr int NUM_XCD = 8;
+constexpr int SBLK = 4;        // K groups per scale block
+constexpr int NSLOT = 3;       // scale blocks resident in LDS
 
 // Workgroup tile BM x BN, WM x WN waves of (BM/WM) x (BN/WN).
 // NSTAGE = 3: fragments of the next K group are read from LDS while the
@@ -67,13 +75,22 @@ struct Cfg {
   static constexpr int NB = BN / WN / 16;         // 16-column blocks per wave
   static constexpr int A_BYTES = BM * 128;
   static constexpr int B_BYTES = BN * 128;
-  static constexpr int S_BYTES = NW * 256;        // one 64-float scale slot per wave
-  static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int DPW = (BM + BN) / 8 / NW;  // 1 KiB tile copies per wave per K group
+  // Scale ring: NSLOT slots, each with the scales of SBLK consecutive K
+  // groups; A scales as [BM/16][SBLK][16] floats, B scales as
+  // [BN/16][SBLK][16] (row mode) or [SBLK][16] (block mode) floats.
+  static constexpr int SAW = BM / 64;             // waves copying A scales
+  static constexpr int SA_BYTES = BM * SBLK * 4;
+  static constexpr int sbw(bool brow) { return brow ? BN / 64 : 1; }
+  static constexpr int sb_bytes(bool brow) { return brow ? BN * SBLK * 4 : 256; }
+  static constexpr int slot_bytes(bool brow) { return SA_BYTES + sb_bytes(brow); }
+  static constexpr int sc_area() { return NSTAGE * STAGE; }
+  static constexpr int dummy_off(bool brow) { return sc_area() + NSLOT * slot_bytes(brow); }
+  static constexpr int lds_bytes(bool brow) { return dummy_off(brow) + 256; }
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
   static_assert((BM + BN) % (8 * NW) == 0, "tile copies must split evenly over the waves");
-  static_assert(BM % 64 == 0 && BN % 64 == 0 && BM / 64 + BN / 64 <= NW, "one scale copy per wave");
-  static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS stages");
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && SAW + BN / 64 <= NW, "one scale copy per wave");
 };
 
 #ifndef FP8BS_GEMM_CFG
@@ -129,20 +146,37 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   nt = rr / gm;
 }
 
-// Direct global -> LDS copies.  global_load_lds_dword{,x4} writes lane l's
-// 4 (16) bytes at M0 + 4 l (16 l); M0 is saved and restored around the copy
-// so no compiler-owned use of M0 is disturbed.  The compiler does not see
-// these as LDS writes: completion is waited for explicitly with vmcnt
-// before the barrier that publishes a stage.
-__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_addr) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "s"(lds_addr), "v"(src) : "memory");
+// Direct global -> LDS copies through buffer descriptors.
+// buffer_load_dword{,x4} ... offen lds writes lane l's 4 (16) bytes at
+// M0 + 4 l (16 l).  The descriptor covers only the valid rows of the tile:
+// a lane whose offset (VGPR offset + SGPR offset) is past the end reads
+// zeros instead of memory, so ragged tiles need no per-lane clamping.  M0 is
+// saved and restored around the copy so no compiler-owned use of M0 is
+// disturbed.  The compiler does not see these as memory operations:
+// completion is waited for explicitly with vmcnt before the barrier that
+// publishes a stage.
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = static_cast<int>(static_cast<uint32_t>(b));
+  r[1] = static_cast<int>(static_cast<uint32_t>(b >> 32) & 0xffffu);  // stride 0: raw buffer
+  r[2] = static_cast<int>(bytes);                                      // bytes in range
+  r[3] = 0x00020000;                                                   // 32-bit data format
+  return r;
 }
-__device__ __forceinline__ void copy4_to_lds(const void* src, uint32_t lds_addr) {
+__device__ __forceinline__ void copy16_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t soff,
+                                              uint32_t lds_addr) {
   uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "s"(lds_addr), "v"(src) : "memory");
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+__device__ __forceinline__ void copy4_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t soff,
+                                             uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dword %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
@@ -161,37 +195,40 @@ struct Frag {
   float sbv;            // block mode: the wave's B block scale
 };
 
+// `slot` is the scale-ring slot holding the group, `gq` the group's index
+// inside its scale block.
 template <class C, bool BROW>
-__device__ __forceinline__ void load_frag(Frag<C>& f, const uint8_t* stage, int wm, int wn, int lane) {
-  constexpr int TM = C::MB * 16, TN = C::NB * 16;
+__device__ __forceinline__ void load_frag(Frag<C>& f, const uint8_t* stage, const float* slot, int gq,
+                                          int wm, int wn, int lane) {
   const uint8_t* la = stage;
   const uint8_t* lb = stage + C::A_BYTES;
-  const float* ls = reinterpret_cast<const float*>(stage + C::A_BYTES + C::B_BYTES);
+  const float* lsb = slot + C::SA_BYTES / 4;
   const int fr = lane & 15;
   const int kc = lane >> 4;  // k chunks kc and kc + 4 (any permutation shared by A and B is valid)
 #pragma unroll
   for (int j = 0; j < C::NB; ++j) {
-    const int r = wn * TN + j * 16 + fr;
+    const int r = (wn * C::NB + j) * 16 + fr;
     const u32x4 lo = *reinterpret_cast<const u32x4*>(lb + swz(r, kc));
     const u32x4 hi = *reinterpret_cast<const u32x4*>(lb + swz(r, kc + 4));
     f.fb[j] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   }
 #pragma unroll
   for (int i = 0; i < C::MB; ++i) {
-    const int r = wm * TM + i * 16 + fr;
+    const int rb = wm * C::MB + i;
+    const int r = rb * 16 + fr;
     const u32x4 lo = *reinterpret_cast<const u32x4*>(la + swz(r, kc));
     const u32x4 hi = *reinterpret_cast<const u32x4*>(la + swz(r, kc + 4));
     f.fa[i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    f.sam[i] = ls[r];
+    f.sam[i] = slot[(rb * SBLK + gq) * 16 + fr];
   }
   if (BROW) {
 #pragma unroll
     for (int j = 0; j < C::NB; ++j) {
-      const float4 v = *reinterpret_cast<const float4*>(ls + C::BM + wn * TN + j * 16 + 4 * kc);
+      const float4 v = *reinterpret_cast<const float4*>(lsb + ((wn * C::NB + j) * SBLK + gq) * 16 + 4 * kc);
       f.sbn[j][0] = v.x; f.sbn[j][1] = v.y; f.sbn[j][2] = v.z; f.sbn[j][3] = v.w;
     }
   } else {
-    f.sbv = ls[C::BM + (wn * TN) / 128];
+    f.sbv = lsb[gq * 16 + (wn * C::NB * 16) / 128];
   }
 }
 
@@ -222,18 +259,17 @@ __device__ __forceinline__ void compute(v4f (&acc)[C::MB][C::NB], const Frag<C>&
 // fragments are read once, the A-tile fragments block by block with the
 // next block's read issued before the current block's MFMAs.
 template <class C, bool BROW>
-__device__ __forceinline__ void compute_lds(v4f (&acc)[C::MB][C::NB], const uint8_t* stage, int wm,
-                                            int wn, int lane) {
-  constexpr int TM = C::MB * 16, TN = C::NB * 16;
+__device__ __forceinline__ void compute_lds(v4f (&acc)[C::MB][C::NB], const uint8_t* stage,
+                                            const float* slot, int gq, int wm, int wn, int lane) {
   const uint8_t* la = stage;
   const uint8_t* lb = stage + C::A_BYTES;
-  const float* ls = reinterpret_cast<const float*>(stage + C::A_BYTES + C::B_BYTES);
+  const float* lsb = slot + C::SA_BYTES / 4;
   const int fr = lane & 15;
   const int kc = lane >> 4;
   v8i fb[C::NB];
 #pragma unroll
   for (int j = 0; j < C::NB; ++j) {
-    const int r = wn * TN + j * 16 + fr;
+    const int r = (wn * C::NB + j) * 16 + fr;
     const u32x4 lo = *reinterpret_cast<const u32x4*>(lb + swz(r, kc));
     const u32x4 hi = *reinterpret_cast<const u32x4*>(lb + swz(r, kc + 4));
     fb[j] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
@@ -243,21 +279,22 @@ __device__ __forceinline__ void compute_lds(v4f (&acc)[C::MB][C::NB], const uint
   if (BROW) {
 #pragma unroll
     for (int j = 0; j < C::NB; ++j) {
-      const float4 v = *reinterpret_cast<const float4*>(ls + C::BM + wn * TN + j * 16 + 4 * kc);
+      const float4 v = *reinterpret_cast<const float4*>(lsb + ((wn * C::NB + j) * SBLK + gq) * 16 + 4 * kc);
       sbn[j][0] = v.x; sbn[j][1] = v.y; sbn[j][2] = v.z; sbn[j][3] = v.w;
     }
   } else {
-    sbv = ls[C::BM + (wn * TN) / 128];
+    sbv = lsb[gq * 16 + (wn * C::NB * 16) / 128];
   }
   __builtin_amdgcn_s_setprio(1);
   __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
   for (int i = 0; i < C::MB; ++i) {
-    const int r = wm * TM + i * 16 + fr;
+    const int rb = wm * C::MB + i;
+    const int r = rb * 16 + fr;
     const u32x4 lo = *reinterpret_cast<const u32x4*>(la + swz(r, kc));
     const u32x4 hi = *reinterpret_cast<const u32x4*>(la + swz(r, kc + 4));
     const v8i fa = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    const float sam = ls[r];
+    const float sam = slot[(rb * SBLK + gq) * 16 + fr];
     const float sc = sam * sbv;
 #pragma unroll
     for (int j = 0; j < C::NB; ++j) {
@@ -275,13 +312,14 @@ __device__ __forceinline__ void compute_lds(v4f (&acc)[C::MB][C::NB], const uint
 template <class C, bool OUT_F32, bool BROW, bool GROUPED>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   constexpr int BM = C::BM, BN = C::BN;
-  __shared__ __align__(16) uint8_t lds[C::NSTAGE * C::STAGE];
+  static_assert(C::lds_bytes(BROW) <= 160 * 1024, "LDS budget");
+  __shared__ __align__(16) uint8_t lds[C::lds_bytes(BROW)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
-  const int64_t G = p.K / 128;
+  const int G = static_cast<int>(p.K / 128);
 
   // ---- tile ------------------------------------------------------------
   int vm, nt;
@@ -296,12 +334,15 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     m0 = -1;
     m_end = 0;
     for (; e < p.E; ++e) {
-      const int64_t r0 = p.offsets[e], r1 = p.offsets[e + 1];
-      const int64_t cnt = r1 - r0;
-      const int64_t tiles = cnt > 0 ? (cnt + BM - 1) / BM : 0;
+      // offsets are clamped into [0, M] so that inconsistent offsets can
+      // only give wrong rows, never an out-of-bounds access
+      int64_t r0 = p.offsets[e], r1 = p.offsets[e + 1];
+      r0 = r0 < 0 ? 0 : (r0 > p.M ? p.M : r0);
+      r1 = r1 < r0 ? r0 : (r1 > p.M ? p.M : r1);
+      const int64_t tiles = (r1 - r0 + BM - 1) / BM;
       if (mt < tiles) {
         m0 = r0 + mt * BM;
-        m_end = r1 < p.M ? r1 : p.M;
+        m_end = r1;
         break;
       }
       mt -= tiles;
@@ -316,63 +357,103 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   // block mode: a wave's columns lie inside one 128-wide block of B
   static_assert(BROW || (128 % (C::NB * 16) == 0), "wave columns must not straddle a B block");
 
-  // ---- copy plan: the tile rows of a K group are DPW 1 KiB copies per
-  //      wave (8 rows each, A rows first, then B rows); lane l fetches the
-  //      global chunk (l & 7) ^ swizzle(row) of row l / 8 of its copy
-  const uint8_t* src[C::DPW];
-  uint32_t dst_off[C::DPW];
-#pragma unroll
-  for (int q = 0; q < C::DPW; ++q) {
-    const int I = wave * C::DPW + q;               // copy index within the K group
-    const bool isA = I < BM / 8;
-    const int r = (isA ? I : I - BM / 8) * 8 + (lane >> 3);  // row inside its tile
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    int64_t grow;
-    if (isA) {
-      grow = m0 + r;
-      grow = grow < m_end ? grow : m_end - 1;
-      src[q] = p.a + grow * p.lda + c * 16;
-    } else {
-      grow = n0 + r;
-      grow = grow < p.N ? grow : p.N - 1;
-      src[q] = bmat + grow * p.ldb + c * 16;
-    }
-    dst_off[q] = isA ? I * 1024 : C::A_BYTES + (I - BM / 8) * 1024;
-  }
-  // one scale copy per wave (64 floats into the wave's slot): A scales of
-  // 64 tile rows, then B scales (row mode: 64 rows; block mode: the column
-  // blocks), the remaining waves re-read a valid A-scale row (unused)
-  const float* ssrc;
+  // ---- tile copy plan: the tile rows of a K group are DPW 1 KiB copies per
+  //      wave; copy q of wave w moves rows 8 (q NW + w) .. 8 (q NW + w) + 7
+  //      of the tile pair (A rows first, then B rows), so whether it is an A
+  //      or a B copy depends on q only, and its rows are the wave's rows of
+  //      copy 0 moved by a multiple of 8 NW rows (a uniform offset).  Lane l
+  //      fetches the global chunk (l & 7) ^ swizzle(row) of row l / 8 of its
+  //      copy; the swizzle does not depend on q.
+  static_assert((BM / 8) % C::NW == 0 && C::NW % 2 == 0, "A copies must be whole rounds over the waves");
+  constexpr int QA = BM / 8 / C::NW;  // copies per wave that move A rows
+  const int64_t rows_a = m_end - m0 < BM ? m_end - m0 : BM;
+  const int64_t rows_b = p.N - n0 < BN ? p.N - n0 : BN;
+  const i32x4 rs_a = make_rsrc(p.a + m0 * p.lda, static_cast<uint32_t>(rows_a * p.lda));
+  const i32x4 rs_b = make_rsrc(bmat + n0 * p.ldb, static_cast<uint32_t>(rows_b * p.ldb));
+  const uint32_t lda = static_cast<uint32_t>(p.lda), ldb = static_cast<uint32_t>(p.ldb);
+  uint32_t voff_a, voff_b;
   {
-    const int SA = BM / 64, SB = BROW ? BN / 64 : 1;
-    if (wave < SA) {
-      int64_t r = m0 + wave * 64 + lane;
-      r = r < m_end ? r : m_end - 1;
-      ssrc = p.sa + r * p.ldsa;
-    } else if (wave < SA + SB) {
+    const int r = 8 * wave + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    voff_a = static_cast<uint32_t>(r) * lda + c * 16;
+    voff_b = static_cast<uint32_t>(r) * ldb + c * 16;
+  }
+
+  // ---- scale copy plan: every issue copies one quarter of a scale block
+  //      (SBLK groups) with one dword copy per wave.  A-scale wave w, quarter
+  //      q covers rows 16 (q SAW + w) .. + 15 (lane l: row + l % 16, group
+  //      SBLK h + l / 16); B-scale waves likewise (row mode) or all the
+  //      tile's 128-row blocks (block mode); the remaining waves re-read a
+  //      valid A scale into a dummy LDS area.
+  i32x4 sc_rs;
+  uint32_t sc_voff, sc_qstep, sc_hstep, sc_dst0, sc_dstq;
+  uint32_t sc_slot = C::slot_bytes(BROW);  // 0 for the dummy copies
+  {
+    constexpr int SAW = C::SAW, SBW = C::sbw(BROW);
+    const uint32_t ldsa4 = static_cast<uint32_t>(p.ldsa * 4), ldsb4 = static_cast<uint32_t>(p.ldsb * 4);
+    const i32x4 rs_sa = make_rsrc(p.sa + m0 * p.ldsa, static_cast<uint32_t>(rows_a) * ldsa4);
+    const uint32_t gl = static_cast<uint32_t>(lane >> 4) * 4u;
+    sc_hstep = SBLK * 4;
+    if (wave < SAW) {
+      sc_rs = rs_sa;
+      sc_voff = static_cast<uint32_t>(16 * wave + (lane & 15)) * ldsa4 + gl;
+      sc_qstep = 16 * SAW * ldsa4;
+      sc_dst0 = wave * 256;
+      sc_dstq = SAW * 256;
+    } else if (wave < SAW + SBW) {
+      const int w = wave - SAW;
       if (BROW) {
-        int64_t r = n0 + (wave - SA) * 64 + lane;
-        r = r < p.N ? r : p.N - 1;
-        ssrc = sbmat + r * p.ldsb;
+        sc_rs = make_rsrc(sbmat + n0 * p.ldsb, static_cast<uint32_t>(rows_b) * ldsb4);
+        sc_voff = static_cast<uint32_t>(16 * w + (lane & 15)) * ldsb4 + gl;
+        sc_qstep = 16 * SBW * ldsb4;
+        sc_dst0 = C::SA_BYTES + w * 256;
+        sc_dstq = SBW * 256;
       } else {
-        int64_t blk = n0 / 128 + lane;
-        const int64_t last_blk = (p.N - 1) / 128;
-        blk = blk < last_blk ? blk : last_blk;
-        ssrc = sbmat + blk * p.ldsb;
+        const int64_t blocks = (rows_b + 127) / 128;
+        sc_rs = make_rsrc(sbmat + (n0 / 128) * p.ldsb, static_cast<uint32_t>(blocks) * ldsb4);
+        sc_voff = static_cast<uint32_t>(lane & 15) * ldsb4 + gl;
+        sc_qstep = 0;
+        sc_dst0 = C::SA_BYTES;
+        sc_dstq = 0;
       }
     } else {
-      ssrc = p.sa + m0 * p.ldsa;
+      sc_rs = rs_sa;
+      sc_voff = 0;
+      sc_qstep = 0;
+      sc_hstep = 0;
+      sc_dst0 = C::dummy_off(BROW) - C::sc_area();
+      sc_dstq = 0;
+      sc_slot = 0;
     }
   }
-  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&lds[0]));
-  const uint32_t s_off = C::A_BYTES + C::B_BYTES + wave * 256;
-  constexpr int COPIES = C::DPW + 1;  // vector-memory ops per wave per K group
 
-  auto issue = [&](int64_t g, int stage) {
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&lds[0]));
+  constexpr int COPIES = C::DPW + 1;  // vector-memory ops per wave per issue
+  constexpr int SLOT = C::slot_bytes(BROW);
+
+  // quarter q of scale block h
+  auto issue_scales = [&](int q, int h) {
+    const uint32_t dst = lds_base + C::sc_area() + (h % NSLOT) * sc_slot + sc_dst0 +
+                         sc_dstq * q;
+    copy4_to_lds(sc_rs, sc_voff, sc_qstep * q + sc_hstep * h, dst);
+  };
+  // issue t: the tile rows of K group min(t, G - 1) into `stage`, and
+  // quarter t % 4 of scale block t / 4 + 1 (block 0 is copied up front)
+  auto issue = [&](int t, int stage) {
+    const uint32_t gk = static_cast<uint32_t>(t < G - 1 ? t : G - 1) * 128u;
     const uint32_t base = lds_base + stage * C::STAGE;
 #pragma unroll
-    for (int q = 0; q < C::DPW; ++q) copy16_to_lds(src[q] + g * 128, base + dst_off[q]);
-    copy4_to_lds(ssrc + g, base + s_off);
+    for (int q = 0; q < C::DPW; ++q) {
+      if (q < QA)
+        copy16_to_lds(rs_a, voff_a, gk + q * (8 * C::NW) * lda, base + (q * C::NW + wave) * 1024);
+      else
+        copy16_to_lds(rs_b, voff_b, gk + (q - QA) * (8 * C::NW) * ldb,
+                      base + C::A_BYTES + ((q - QA) * C::NW + wave) * 1024);
+    }
+    issue_scales(t & 3, (t >> 2) + 1);
+  };
+  auto slot_of = [&](int g) {
+    return reinterpret_cast<const float*>(lds + C::sc_area() + ((g / SBLK) % NSLOT) * SLOT);
   };
 
   v4f acc[C::MB][C::NB];
@@ -381,41 +462,44 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < C::NB; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int64_t last = G - 1;
-  auto clampg = [&](int64_t x) { return x < last ? x : last; };
+#pragma unroll
+  for (int q = 0; q < SBLK; ++q) issue_scales(q, 0);
   if constexpr (C::NSTAGE == 3) {
     // Pipeline over three stages, stage(x) = x % 3.  Before iteration g:
     // fragments of group g are in registers (cur), stage(g + 1) holds group
     // g + 1 and is visible, the copy of group g + 2 into stage(g + 2) is in
-    // flight.  Iteration g reads the fragments of g + 1, starts the copy of
-    // g + 3 into stage(g) (whose reads finished before the last barrier),
-    // multiplies g, then waits for the copy of g + 2 and for its own LDS
-    // reads before the barrier.  Copies and reads past the last group are
-    // clamped to the last group: they move valid data that is never used.
+    // flight.  Iteration g reads the fragments of g + 1, starts issue g + 3
+    // into stage(g) (whose reads finished before the last barrier),
+    // multiplies g, then waits for issue g + 2 and for its own LDS reads
+    // before the barrier.  Scale block h is copied by issues 4h - 4 ..
+    // 4h - 1 (iterations 4h - 7 .. 4h - 4), is first read in iteration
+    // 4h - 1, and its slot was last read in iteration 4h - 10.  Copies and
+    // reads past the last group are clamped to valid data that is never
+    // used.
     issue(0, 0);
-    issue(clampg(1), 1);
+    issue(1, 1);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     block_barrier();
     Frag<C> f0, f1;
-    load_frag<C, BROW>(f0, lds, wm, wn, lane);
+    load_frag<C, BROW>(f0, lds, slot_of(0), 0, wm, wn, lane);
     __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
-    issue(clampg(2), 2);
+    issue(2, 2);
     block_barrier();
 
-    int64_t g = 0;
+    int g = 0;
     int st1 = 1;  // stage(g + 1)
     for (; g + 2 <= G; g += 2) {
       // iteration g: cur = f0, next = f1
-      load_frag<C, BROW>(f1, lds + st1 * C::STAGE, wm, wn, lane);
-      issue(clampg(g + 3), st1 == 0 ? 2 : st1 - 1);
+      load_frag<C, BROW>(f1, lds + st1 * C::STAGE, slot_of(g + 1), (g + 1) & 3, wm, wn, lane);
+      issue(g + 3, st1 == 0 ? 2 : st1 - 1);
       compute<C, BROW>(acc, f0);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(COPIES));
       __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
       block_barrier();
       st1 = st1 == 2 ? 0 : st1 + 1;
       // iteration g + 1: cur = f1, next = f0
-      load_frag<C, BROW>(f0, lds + st1 * C::STAGE, wm, wn, lane);
-      issue(clampg(g + 4), st1 == 0 ? 2 : st1 - 1);
+      load_frag<C, BROW>(f0, lds + st1 * C::STAGE, slot_of(g + 2), (g + 2) & 3, wm, wn, lane);
+      issue(g + 4, st1 == 0 ? 2 : st1 - 1);
       compute<C, BROW>(acc, f1);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(COPIES));
       __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
@@ -425,17 +509,19 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     if (g < G)  // odd G: the last group's fragments are in f0
       compute<C, BROW>(acc, f0);
   } else {
-    // Two stages, stage(x) = x % 2.  Iteration g starts the copy of g + 1
-    // into the other stage (read during iteration g - 1, finished before
-    // the last barrier), multiplies g straight from LDS, then waits for the
-    // copy and its own reads before the barrier.
+    // Two stages, stage(x) = x % 2.  Iteration g starts issue g + 1 into
+    // the other stage (read during iteration g - 1, finished before the last
+    // barrier), multiplies g straight from LDS, then waits for the copies
+    // and its own reads before the barrier.  Scale block h is copied by
+    // issues 4h - 4 .. 4h - 1 (iterations 4h - 5 .. 4h - 2) and first read
+    // in iteration 4h.
     issue(0, 0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     block_barrier();
-    for (int64_t g = 0; g < G; ++g) {
-      const int st = static_cast<int>(g & 1);
-      issue(clampg(g + 1), st ^ 1);
-      compute_lds<C, BROW>(acc, lds + st * C::STAGE, wm, wn, lane);
+    for (int g = 0; g < G; ++g) {
+      const int st = g & 1;
+      issue(g + 1, st ^ 1);
+      compute_lds<C, BROW>(acc, lds + st * C::STAGE, slot_of(g), g & 3, wm, wn, lane);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
       block_barrier();

@@ -125,7 +125,8 @@ fp8bs_status fp8bs_requant_T_128x1(fp8bs_requant_src src, const void *in, const 
  *   b   u8  [N][ldb]      sb f32, layout by bmode (see fp8bs_bscale)
  *   d   bf16 or f32 [M][ldd]
  * M, N >= 0 (either 0 is a no-op); K > 0, K % 128 == 0.  M and N may be
- * ragged.
+ * ragged.  lda, ldb < 2^24 and ldsa, ldsb < 2^22, else
+ * FP8BS_ERR_UNSUPPORTED_SHAPE.
  */
 fp8bs_status fp8bs_gemm(const uint8_t *a, const float *sa, int64_t lda, int64_t ldsa,
                         const uint8_t *b, const float *sb, int64_t ldb, int64_t ldsb,
@@ -144,7 +145,8 @@ fp8bs_status fp8bs_gemm(const uint8_t *a, const float *sa, int64_t lda, int64_t 
  *            violation gives unspecified rows but no out-of-bounds access)
  *   d        bf16 or f32 [M_total][N] (dense)
  * M_total sizes the launch only; no host synchronization.
- * E >= 1, M_total >= 0, N > 0, K > 0, K % 128 == 0.
+ * E >= 1, M_total >= 0, N > 0, K > 0, K % 128 == 0; K < 2^24 and
+ * ldsa < 2^22, else FP8BS_ERR_UNSUPPORTED_SHAPE.
  */
 fp8bs_status fp8bs_grouped_gemm(const uint8_t *a, const float *sa, int64_t ldsa,
                                 const uint8_t *b, const float *sb,

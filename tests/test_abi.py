@@ -95,6 +95,8 @@ def grouped(a=A, sa=A, ldsa=2, b=A, sb=A, off=A, E=2, M=10, d=A, dt=0, N=128, K=
     (lambda: gemm(lda=264), fp8bs.ERR_MISALIGNED),
     (lambda: gemm(d=A + 4), fp8bs.ERR_MISALIGNED),
     (lambda: gemm(ldd=68), fp8bs.ERR_MISALIGNED),
+    (lambda: gemm(lda=1 << 24), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: gemm(ldsb=1 << 22), fp8bs.ERR_UNSUPPORTED_SHAPE),
     (lambda: gemm(M=0), fp8bs.OK),
     (lambda: gemm(N=0), fp8bs.OK),
     (lambda: grouped(E=0), fp8bs.ERR_INVALID_ARG),
@@ -103,6 +105,8 @@ def grouped(a=A, sa=A, ldsa=2, b=A, sb=A, off=A, E=2, M=10, d=A, dt=0, N=128, K=
     (lambda: grouped(K=100), fp8bs.ERR_UNSUPPORTED_SHAPE),
     (lambda: grouped(N=0), fp8bs.ERR_INVALID_ARG),
     (lambda: grouped(N=68), fp8bs.ERR_MISALIGNED),
+    (lambda: grouped(K=1 << 24, ldsa=1 << 17), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: grouped(ldsa=1 << 22), fp8bs.ERR_UNSUPPORTED_SHAPE),
     (lambda: grouped(M=0), fp8bs.OK),
 ])
 def test_argument_checks_before_any_hip_call(call, expect):
