@@ -255,6 +255,92 @@ __device__ __forceinline__ void compute(v4f (&acc)[C::MB][C::NB], const Frag<C>&
   __builtin_amdgcn_s_setprio(0);
 }
 
+// Software-pipelined K group for the three-stage path.  The MFMAs of the
+// current group are issued one per step; each step also promotes the
+// partial of the MFMA issued LAG steps earlier, issues one read of the next
+// group's fragments from LDS, and every other step one global -> LDS copy,
+// so the LDS and the load unit see a steady stream instead of a burst
+// after each barrier.  A scheduling barrier after every step keeps that
+// placement.
+constexpr int LAG = 2;
+
+// Read number k of the next group's fragments: B rows, A rows, A scales,
+// then the B scales.
+template <class C, bool BROW>
+__device__ __forceinline__ void read_op(Frag<C>& f, int k, const uint8_t* stage, const float* slot,
+                                        int gq, int wm, int wn, int lane) {
+  const uint8_t* la = stage;
+  const uint8_t* lb = stage + C::A_BYTES;
+  const float* lsb = slot + C::SA_BYTES / 4;
+  const int fr = lane & 15;
+  const int kc = lane >> 4;
+  if (k < C::NB) {
+    const int r = (wn * C::NB + k) * 16 + fr;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(lb + swz(r, kc));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(lb + swz(r, kc + 4));
+    f.fb[k] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  } else if (k < C::NB + C::MB) {
+    const int i = k - C::NB;
+    const int r = (wm * C::MB + i) * 16 + fr;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(la + swz(r, kc));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(la + swz(r, kc + 4));
+    f.fa[i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  } else if (k < C::NB + 2 * C::MB) {
+    const int i = k - C::NB - C::MB;
+    f.sam[i] = slot[((wm * C::MB + i) * SBLK + gq) * 16 + fr];
+  } else if (BROW) {
+    const int j = k - C::NB - 2 * C::MB;
+    const float4 v = *reinterpret_cast<const float4*>(lsb + ((wn * C::NB + j) * SBLK + gq) * 16 + 4 * kc);
+    f.sbn[j][0] = v.x; f.sbn[j][1] = v.y; f.sbn[j][2] = v.z; f.sbn[j][3] = v.w;
+  } else {
+    f.sbv = lsb[gq * 16 + (wn * C::NB * 16) / 128];
+  }
+}
+
+template <class C, bool BROW>
+constexpr int read_ops() { return C::NB + 2 * C::MB + (BROW ? C::NB : 1); }
+
+template <class C, bool BROW>
+__device__ __forceinline__ void promote(v4f (&acc)[C::MB][C::NB], const v4f& part, int s,
+                                        const Frag<C>& f) {
+  const int i = s / C::NB, j = s % C::NB;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float sc = BROW ? f.sam[i] * f.sbn[j][q] : f.sam[i] * f.sbv;
+    acc[i][j][q] = __builtin_fmaf(part[q], sc, acc[i][j][q]);
+  }
+}
+
+// issue_part(k) issues copy k of the next issue (k < copies).
+template <class C, bool BROW, int COPIES, class IssuePart>
+__device__ __forceinline__ void pipelined_group(v4f (&acc)[C::MB][C::NB], const Frag<C>& cur,
+                                                Frag<C>& nxt, const uint8_t* stage_n,
+                                                const float* slot_n, int gq_n, int wm, int wn,
+                                                int lane, IssuePart&& issue_part) {
+  constexpr int S = C::MB * C::NB;
+  constexpr int NR = read_ops<C, BROW>();
+  static_assert(S >= 2, "steps");
+  v4f part[S];
+  __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+  for (int s = 0; s < S + LAG; ++s) {
+    if (s < S) part[s] = mfma_16x16x128_fp8(cur.fb[s % C::NB], cur.fa[s / C::NB]);
+    if (s >= LAG) promote<C, BROW>(acc, part[s - LAG], s - LAG, cur);
+    // reads k in [s NR / S, (s + 1) NR / S); copies spread over steps 1 .. S - 1
+    if (s < S) {
+#pragma unroll
+      for (int k = s * NR / S; k < (s + 1) * NR / S; ++k)
+        read_op<C, BROW>(nxt, k, stage_n, slot_n, gq_n, wm, wn, lane);
+    }
+    if (s >= 1 && s < S) {
+#pragma unroll
+      for (int k = (s - 1) * COPIES / (S - 1); k < s * COPIES / (S - 1); ++k) issue_part(k);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
+
 // One K group straight from an LDS stage (two-stage pipeline): the B-tile
 // fragments are read once, the A-tile fragments block by block with the
 // next block's read issued before the current block's MFMAs.
@@ -437,6 +523,20 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
                          sc_dstq * q;
     copy4_to_lds(sc_rs, sc_voff, sc_qstep * q + sc_hstep * h, dst);
   };
+  // part k of issue t: tile copy k (k < DPW) of K group min(t, G - 1) into
+  // `stage`, or (k == DPW) quarter t % 4 of scale block t / 4 + 1 (block 0
+  // is copied up front)
+  auto issue_part = [&](int t, int stage, int k) {
+    const uint32_t gk = static_cast<uint32_t>(t < G - 1 ? t : G - 1) * 128u;
+    const uint32_t base = lds_base + stage * C::STAGE;
+    if (k < QA)
+      copy16_to_lds(rs_a, voff_a, gk + k * (8 * C::NW) * lda, base + (k * C::NW + wave) * 1024);
+    else if (k < C::DPW)
+      copy16_to_lds(rs_b, voff_b, gk + (k - QA) * (8 * C::NW) * ldb,
+                    base + C::A_BYTES + ((k - QA) * C::NW + wave) * 1024);
+    else
+      issue_scales(t & 3, (t >> 2) + 1);
+  };
   // issue t: the tile rows of K group min(t, G - 1) into `stage`, and
   // quarter t % 4 of scale block t / 4 + 1 (block 0 is copied up front)
   auto issue = [&](int t, int stage) {
@@ -490,17 +590,21 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     int st1 = 1;  // stage(g + 1)
     for (; g + 2 <= G; g += 2) {
       // iteration g: cur = f0, next = f1
-      load_frag<C, BROW>(f1, lds + st1 * C::STAGE, slot_of(g + 1), (g + 1) & 3, wm, wn, lane);
-      issue(g + 3, st1 == 0 ? 2 : st1 - 1);
-      compute<C, BROW>(acc, f0);
+      {
+        const int t = g + 3, st = st1 == 0 ? 2 : st1 - 1;
+        pipelined_group<C, BROW, COPIES>(acc, f0, f1, lds + st1 * C::STAGE, slot_of(g + 1), (g + 1) & 3,
+                                         wm, wn, lane, [&](int k) { issue_part(t, st, k); });
+      }
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(COPIES));
       __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
       block_barrier();
       st1 = st1 == 2 ? 0 : st1 + 1;
       // iteration g + 1: cur = f1, next = f0
-      load_frag<C, BROW>(f0, lds + st1 * C::STAGE, slot_of(g + 2), (g + 2) & 3, wm, wn, lane);
-      issue(g + 4, st1 == 0 ? 2 : st1 - 1);
-      compute<C, BROW>(acc, f1);
+      {
+        const int t = g + 4, st = st1 == 0 ? 2 : st1 - 1;
+        pipelined_group<C, BROW, COPIES>(acc, f1, f0, lds + st1 * C::STAGE, slot_of(g + 2), (g + 2) & 3,
+                                         wm, wn, lane, [&](int k) { issue_part(t, st, k); });
+      }
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(COPIES));
       __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
       block_barrier();
