@@ -90,7 +90,7 @@ struct Cfg {
   static constexpr int lds_bytes(bool brow) { return dummy_off(brow) + 256; }
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
   static_assert((BM + BN) % (8 * NW) == 0, "tile copies must split evenly over the waves");
-  static_assert(BM % 64 == 0 && BN % 64 == 0 && SAW + BN / 64 <= NW, "one scale copy per wave");
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "scale copies move 16-row units, SBLK per lane row");
 };
 
 #ifndef FP8BS_GEMM_CFG
@@ -102,8 +102,10 @@ using MainCfg = Cfg<256, 128, 4, 2>;
 using MainCfg = Cfg<128, 128, 2, 2>;
 #elif FP8BS_GEMM_CFG == 2
 using MainCfg = Cfg<128, 256, 2, 4>;
-#else
+#elif FP8BS_GEMM_CFG == 3
 using MainCfg = Cfg<256, 256, 2, 4, 2>;
+#else
+using MainCfg = Cfg<256, 128, 2, 2, 3>;
 #endif
 // Row-scale mode holds 16 more scales per fragment set: narrower wave tiles.
 using RowCfg = Cfg<128, 128, 2, 4>;
@@ -466,62 +468,73 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   }
 
   // ---- scale copy plan: every issue copies one quarter of a scale block
-  //      (SBLK groups) with one dword copy per wave.  A-scale wave w, quarter
-  //      q covers rows 16 (q SAW + w) .. + 15 (lane l: row + l % 16, group
-  //      SBLK h + l / 16); B-scale waves likewise (row mode) or all the
-  //      tile's 128-row blocks (block mode); the remaining waves re-read a
-  //      valid A scale into a dummy LDS area.
-  i32x4 sc_rs;
-  uint32_t sc_voff, sc_qstep, sc_hstep, sc_dst0, sc_dstq;
-  uint32_t sc_slot = C::slot_bytes(BROW);  // 0 for the dummy copies
+  //      (SBLK groups).  The quarter is split into units of 16 rows x SBLK
+  //      groups, one dword copy each: SAW units of A scales, then SBW units
+  //      of B scales (row mode: 16 rows each; block mode: all the tile's
+  //      128-row blocks).  Wave w issues units w, w + NW, ... (SPW per
+  //      wave); units past the last re-read a valid A scale into a dummy
+  //      LDS area.  A-scale unit c, quarter q covers rows 16 (q SAW + c) ..
+  //      + 15 (lane l: row + l % 16, group SBLK h + l / 16).
+  constexpr int SAW = C::SAW, SBW = C::sbw(BROW);
+  constexpr int SPW = (SAW + SBW + C::NW - 1) / C::NW;  // scale copies per wave per issue
+  struct ScaleCopy {
+    i32x4 rs;
+    uint32_t voff, qstep, hstep, dst0, dstq, slot;
+  };
+  ScaleCopy sc[SPW];
   {
-    constexpr int SAW = C::SAW, SBW = C::sbw(BROW);
     const uint32_t ldsa4 = static_cast<uint32_t>(p.ldsa * 4), ldsb4 = static_cast<uint32_t>(p.ldsb * 4);
     const i32x4 rs_sa = make_rsrc(p.sa + m0 * p.ldsa, static_cast<uint32_t>(rows_a) * ldsa4);
     const uint32_t gl = static_cast<uint32_t>(lane >> 4) * 4u;
-    sc_hstep = SBLK * 4;
-    if (wave < SAW) {
-      sc_rs = rs_sa;
-      sc_voff = static_cast<uint32_t>(16 * wave + (lane & 15)) * ldsa4 + gl;
-      sc_qstep = 16 * SAW * ldsa4;
-      sc_dst0 = wave * 256;
-      sc_dstq = SAW * 256;
-    } else if (wave < SAW + SBW) {
-      const int w = wave - SAW;
-      if (BROW) {
-        sc_rs = make_rsrc(sbmat + n0 * p.ldsb, static_cast<uint32_t>(rows_b) * ldsb4);
-        sc_voff = static_cast<uint32_t>(16 * w + (lane & 15)) * ldsb4 + gl;
-        sc_qstep = 16 * SBW * ldsb4;
-        sc_dst0 = C::SA_BYTES + w * 256;
-        sc_dstq = SBW * 256;
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+      const int c = wave + u * C::NW;
+      ScaleCopy& x = sc[u];
+      x.hstep = SBLK * 4;
+      x.slot = C::slot_bytes(BROW);
+      if (c < SAW) {
+        x.rs = rs_sa;
+        x.voff = static_cast<uint32_t>(16 * c + (lane & 15)) * ldsa4 + gl;
+        x.qstep = 16 * SAW * ldsa4;
+        x.dst0 = c * 256;
+        x.dstq = SAW * 256;
+      } else if (c < SAW + SBW) {
+        const int w = c - SAW;
+        if (BROW) {
+          x.rs = make_rsrc(sbmat + n0 * p.ldsb, static_cast<uint32_t>(rows_b) * ldsb4);
+          x.voff = static_cast<uint32_t>(16 * w + (lane & 15)) * ldsb4 + gl;
+          x.qstep = 16 * SBW * ldsb4;
+          x.dst0 = C::SA_BYTES + w * 256;
+          x.dstq = SBW * 256;
+        } else {
+          const int64_t blocks = (rows_b + 127) / 128;
+          x.rs = make_rsrc(sbmat + (n0 / 128) * p.ldsb, static_cast<uint32_t>(blocks) * ldsb4);
+          x.voff = static_cast<uint32_t>(lane & 15) * ldsb4 + gl;
+          x.qstep = 0;
+          x.dst0 = C::SA_BYTES;
+          x.dstq = 0;
+        }
       } else {
-        const int64_t blocks = (rows_b + 127) / 128;
-        sc_rs = make_rsrc(sbmat + (n0 / 128) * p.ldsb, static_cast<uint32_t>(blocks) * ldsb4);
-        sc_voff = static_cast<uint32_t>(lane & 15) * ldsb4 + gl;
-        sc_qstep = 0;
-        sc_dst0 = C::SA_BYTES;
-        sc_dstq = 0;
+        x.rs = rs_sa;
+        x.voff = 0;
+        x.qstep = 0;
+        x.hstep = 0;
+        x.dst0 = C::dummy_off(BROW) - C::sc_area();
+        x.dstq = 0;
+        x.slot = 0;
       }
-    } else {
-      sc_rs = rs_sa;
-      sc_voff = 0;
-      sc_qstep = 0;
-      sc_hstep = 0;
-      sc_dst0 = C::dummy_off(BROW) - C::sc_area();
-      sc_dstq = 0;
-      sc_slot = 0;
     }
   }
 
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&lds[0]));
-  constexpr int COPIES = C::DPW + 1;  // vector-memory ops per wave per issue
+  constexpr int COPIES = C::DPW + SPW;  // vector-memory ops per wave per issue
   constexpr int SLOT = C::slot_bytes(BROW);
 
-  // quarter q of scale block h
-  auto issue_scales = [&](int q, int h) {
-    const uint32_t dst = lds_base + C::sc_area() + (h % NSLOT) * sc_slot + sc_dst0 +
-                         sc_dstq * q;
-    copy4_to_lds(sc_rs, sc_voff, sc_qstep * q + sc_hstep * h, dst);
+  // this wave's copy u of quarter q of scale block h
+  auto issue_scales = [&](int u, int q, int h) {
+    const ScaleCopy& x = sc[u];
+    const uint32_t dst = lds_base + C::sc_area() + (h % NSLOT) * x.slot + x.dst0 + x.dstq * q;
+    copy4_to_lds(x.rs, x.voff, x.qstep * q + x.hstep * h, dst);
   };
   // part k of issue t: tile copy k (k < DPW) of K group min(t, G - 1) into
   // `stage`, or (k == DPW) quarter t % 4 of scale block t / 4 + 1 (block 0
@@ -535,7 +548,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
       copy16_to_lds(rs_b, voff_b, gk + (k - QA) * (8 * C::NW) * ldb,
                     base + C::A_BYTES + ((k - QA) * C::NW + wave) * 1024);
     else
-      issue_scales(t & 3, (t >> 2) + 1);
+      issue_scales(k - C::DPW, t & 3, (t >> 2) + 1);
   };
   // issue t: the tile rows of K group min(t, G - 1) into `stage`, and
   // quarter t % 4 of scale block t / 4 + 1 (block 0 is copied up front)
@@ -550,7 +563,8 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
         copy16_to_lds(rs_b, voff_b, gk + (q - QA) * (8 * C::NW) * ldb,
                       base + C::A_BYTES + ((q - QA) * C::NW + wave) * 1024);
     }
-    issue_scales(t & 3, (t >> 2) + 1);
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) issue_scales(u, t & 3, (t >> 2) + 1);
   };
   auto slot_of = [&](int g) {
     return reinterpret_cast<const float*>(lds + C::sc_area() + ((g / SBLK) % NSLOT) * SLOT);
@@ -563,7 +577,9 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     for (int j = 0; j < C::NB; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
 #pragma unroll
-  for (int q = 0; q < SBLK; ++q) issue_scales(q, 0);
+  for (int q = 0; q < SBLK; ++q)
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) issue_scales(u, q, 0);
   if constexpr (C::NSTAGE == 3) {
     // Pipeline over three stages, stage(x) = x % 3.  Before iteration g:
     // fragments of group g are in registers (cur), stage(g + 1) holds group
