@@ -21,6 +21,7 @@ std::atomic<int> g_dev_state[kMaxDevices];
 // 4 GiB, so that 32-bit offsets from its first row reach every element.
 constexpr int64_t kMaxCodeStride = int64_t(1) << 24;   // bytes per code row
 constexpr int64_t kMaxScaleStride = int64_t(1) << 22;  // floats per scale row
+constexpr int64_t kMaxRequantStride = int64_t(1) << 25;  // bytes per input row of requant
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -132,6 +133,9 @@ fp8bs_status fp8bs_requant_T_128x1(fp8bs_requant_src src, const void* in, const 
   if (!bf16) FP8BS_TRY(check_scales(s_in, C / 128, lds_in));
   FP8BS_TRY(check_matrix(q_out, T, ld_out, 1));
   FP8BS_TRY(check_scales(s_out, (T + 127) / 128, lds_out));
+  // 128-token tiles are addressed with 32-bit offsets from their first row
+  if (ld_in * (bf16 ? 2 : 1) >= kMaxRequantStride || (!bf16 && lds_in >= kMaxScaleStride))
+    return FP8BS_ERR_UNSUPPORTED_SHAPE;
   FP8BS_TRY(check_device());
   return launched(fp8bs::launch_requant_T_128x1(bf16, in, s_in, T, C, ld_in, lds_in, q_out, ld_out,
                                                 s_out, lds_out, static_cast<hipStream_t>(stream)));

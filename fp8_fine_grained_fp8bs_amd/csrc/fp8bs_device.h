@@ -153,4 +153,45 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Direct global -> LDS copies through buffer descriptors.
+// buffer_load_dword{,x4} ... offen lds writes lane l's 4 (16) bytes at
+// M0 + 4 l (16 l).  The descriptor covers only the valid rows of the tile:
+// a lane whose offset (VGPR offset + SGPR offset) is past the end reads
+// zeros instead of memory, so ragged tiles need no per-lane clamping.  M0 is
+// saved and restored around the copy so no compiler-owned use of M0 is
+// disturbed.  The compiler does not see these as memory operations:
+// completion is waited for explicitly with vmcnt before the barrier that
+// publishes a stage.
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = static_cast<int>(static_cast<uint32_t>(b));
+  r[1] = static_cast<int>(static_cast<uint32_t>(b >> 32) & 0xffffu);  // stride 0: raw buffer
+  r[2] = static_cast<int>(bytes);                                      // bytes in range
+  r[3] = 0x00020000;                                                   // 32-bit data format
+  return r;
+}
+__device__ __forceinline__ void copy16_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t soff,
+                                              uint32_t lds_addr) {
+  uint32_t saved;
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);  // uniform by contract
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+__device__ __forceinline__ void copy4_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t soff,
+                                             uint32_t lds_addr) {
+  uint32_t saved;
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);  // uniform by contract
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dword %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int WAIT_LGKM0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 }  // namespace fp8bs

@@ -15,15 +15,92 @@ namespace fp8bs {
 namespace {
 
 // ---------------------------------------------------------------------
-// 1x128 activation tiles.  One wave per row; a 16-lane DPP row per tile,
-// 8 bf16 (16 bytes) per lane, so one wave instruction moves 4 consecutive
-// tiles (1 KiB, fully coalesced).  All U tile-quads of a pass (up to the
-// whole row) are loaded before any is processed, so a wave keeps up to
-// U KiB in flight: enough to cover HBM latency even when the grid is one
-// wave per row and the rows are few.
+// 1x128 activation tiles.  A 16-lane DPP row handles one tile, 8 bf16
+// (16 bytes) per lane, so one wave instruction moves 4 consecutive tiles
+// (1 KiB, coalesced).  A work item is U such tile-quads of one row; each
+// wave walks the items gw, gw + nw, gw + 2 nw, ... and loads item i + nw
+// while it encodes and stores item i, so loads and stores of a wave overlap
+// and a small matrix still keeps many requests in flight.
 // ---------------------------------------------------------------------
+// item -> row (32-bit division while the item index fits)
+__device__ __forceinline__ int64_t row_of(int64_t it, int chunks) {
+  if (it <= 0xffffffffll) return static_cast<uint32_t>(it) / static_cast<uint32_t>(chunks);
+  return it / chunks;
+}
+
 template <int U>
-__global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x, int64_t M,
+__device__ __forceinline__ void act_load(const uint16_t* __restrict__ x, int64_t ldx, int G, int chunks,
+                                         int64_t it, int sub, int grp, u32x4 (&v)[U]) {
+  const int64_t row = row_of(it, chunks);
+  const int c = static_cast<int>(it - row * chunks);
+  const uint16_t* xr = x + row * ldx + sub * 8;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int g = (c * U + u) * 4 + grp;
+    if (g < G) {
+      const uint4 t = load16_nt(xr + static_cast<int64_t>(g) * 128);
+      v[u] = u32x4{t.x, t.y, t.z, t.w};
+    } else {
+      v[u] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+template <int U>
+__device__ __forceinline__ void act_encode(uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s,
+                                           int64_t lds, int G, int chunks, int64_t it, int sub,
+                                           int grp, const u32x4 (&v)[U]) {
+  const int64_t row = row_of(it, chunks);
+  const int c = static_cast<int>(it - row * chunks);
+  uint8_t* qr = q + row * ldq + sub * 8;
+  float* sr = s + row * lds;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int g = (c * U + u) * 4 + grp;
+    float f[8] = {bf16_lo(v[u][0]), bf16_hi(v[u][0]), bf16_lo(v[u][1]), bf16_hi(v[u][1]),
+                  bf16_lo(v[u][2]), bf16_hi(v[u][2]), bf16_lo(v[u][3]), bf16_hi(v[u][3])};
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = __builtin_fmaxf(am, __builtin_fabsf(f[i]));
+    am = row16_max(am);
+    const TileScale t = make_tile_scale(am);
+    uint2 cw;
+    cw.x = encode4(f, t);
+    cw.y = encode4(f + 4, t);
+    if (g < G) {
+      *reinterpret_cast<uint2*>(qr + static_cast<int64_t>(g) * 128) = cw;
+      if (sub == 0) sr[g] = t.s;
+    }
+  }
+}
+
+template <int U>
+__global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x, int G,
+                                                        int64_t ldx, uint8_t* __restrict__ q,
+                                                        int64_t ldq, float* __restrict__ s,
+                                                        int64_t lds, int64_t items, int chunks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * 4;
+  const int sub = lane & 15;
+  const int grp = lane >> 4;
+  u32x4 va[U], vb[U];
+  int64_t it = gw;
+  if (it < items) act_load<U>(x, ldx, G, chunks, it, sub, grp, va);
+  for (; it < items; it += 2 * nw) {
+    const int64_t it2 = it + nw, it3 = it2 + nw;
+    if (it2 < items) act_load<U>(x, ldx, G, chunks, it2, sub, grp, vb);
+    act_encode<U>(q, ldq, s, lds, G, chunks, it, sub, grp, va);
+    if (it3 < items) act_load<U>(x, ldx, G, chunks, it3, sub, grp, va);
+    if (it2 < items) act_encode<U>(q, ldq, s, lds, G, chunks, it2, sub, grp, vb);
+  }
+}
+
+// One wave per row, all of the row's tile-quads loaded before any is
+// encoded (up to U KiB in flight per wave): the better shape once the
+// matrix is large enough to keep every compute unit busy for several rows.
+template <int U>
+__global__ __launch_bounds__(256) void quant_act_row_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                         int G, int64_t ldx, uint8_t* __restrict__ q,
                                                         int64_t ldq, float* __restrict__ s,
                                                         int64_t lds) {
@@ -127,28 +204,48 @@ __global__ __launch_bounds__(256) void quant_w_kernel(const uint16_t* __restrict
 
 }  // namespace
 
+// Persistent form: 2 tile-quads per work item, 32 waves per compute unit
+// of a 256-CU MI355X.
+template <int U>
+hipError_t launch_act(const uint16_t* x, int64_t M, int G, int64_t ldx, uint8_t* q, int64_t ldq,
+                      float* s, int64_t lds, hipStream_t st) {
+  const int quads = (G + 3) / 4;
+  const int chunks = (quads + U - 1) / U;
+  const int64_t items = M * chunks;
+  int64_t blocks = (items + 3) / 4;
+  const int64_t cap = 256 * 32 / 4;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(quant_act_kernel<U>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, x, G,
+                     ldx, q, ldq, s, lds, items, chunks);
+  return hipGetLastError();
+}
+
+template <int U>
+hipError_t launch_act_rows(const uint16_t* x, int64_t M, int G, int64_t ldx, uint8_t* q,
+                           int64_t ldq, float* s, int64_t lds, hipStream_t st) {
+  const int64_t blocks = (M + 3) / 4;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_act_row_kernel<U>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                     x, M, G, ldx, q, ldq, s, lds);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_act_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                   uint8_t* q, int64_t ldq, float* s, int64_t lds,
                                   hipStream_t st) {
+  if (K / 128 > (1 << 30)) return hipErrorInvalidValue;
   const int G = static_cast<int>(K / 128);
-  const int64_t blocks = (M + 3) / 4;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
-  // quads of tiles per pass: the whole row when it has at most 64 tiles
   const int quads = (G + 3) / 4;
-  if (quads <= 1)
-    hipLaunchKernelGGL(quant_act_kernel<1>, grid, block, 0, st, x, M, G, ldx, q, ldq, s, lds);
-  else if (quads <= 2)
-    hipLaunchKernelGGL(quant_act_kernel<2>, grid, block, 0, st, x, M, G, ldx, q, ldq, s, lds);
-  else if (quads <= 4)
-    hipLaunchKernelGGL(quant_act_kernel<4>, grid, block, 0, st, x, M, G, ldx, q, ldq, s, lds);
-  else if (quads <= 8)
-    hipLaunchKernelGGL(quant_act_kernel<8>, grid, block, 0, st, x, M, G, ldx, q, ldq, s, lds);
-  else if (quads <= 14)
-    hipLaunchKernelGGL(quant_act_kernel<14>, grid, block, 0, st, x, M, G, ldx, q, ldq, s, lds);
-  else
-    hipLaunchKernelGGL(quant_act_kernel<16>, grid, block, 0, st, x, M, G, ldx, q, ldq, s, lds);
-  return hipGetLastError();
+  // Long rows, up to 64K two-quad items: the persistent form (the loads of
+  // the next item overlap the encoding of the current one); otherwise one
+  // wave per row.
+  if (quads >= 8 && M * ((quads + 1) / 2) <= 65536) return launch_act<2>(x, M, G, ldx, q, ldq, s, lds, st);
+  if (quads <= 1) return launch_act_rows<1>(x, M, G, ldx, q, ldq, s, lds, st);
+  if (quads <= 2) return launch_act_rows<2>(x, M, G, ldx, q, ldq, s, lds, st);
+  if (quads <= 4) return launch_act_rows<4>(x, M, G, ldx, q, ldq, s, lds, st);
+  if (quads <= 8) return launch_act_rows<8>(x, M, G, ldx, q, ldq, s, lds, st);
+  if (quads <= 14) return launch_act_rows<14>(x, M, G, ldx, q, ldq, s, lds, st);
+  return launch_act_rows<16>(x, M, G, ldx, q, ldq, s, lds, st);
 }
 
 hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,

@@ -105,7 +105,9 @@ fp8bs_status fp8bs_quant_w_128x128(const void *w, int64_t N, int64_t K, int64_t 
  *   q_out  u8  [C][ld_out]            q_out[c*ld_out + t]
  *   s_out  f32 [C][lds_out]           s_out[c*lds_out + t/128], ceil(T/128) per row
  * T may be ragged (the last token tile takes its max-abs over the tokens
- * present).  T >= 0, C > 0, C % 128 == 0.
+ * present).  T >= 0, C > 0, C % 128 == 0; an input row must span fewer
+ * than 2^25 bytes (ld_in) and lds_in < 2^22, else
+ * FP8BS_ERR_UNSUPPORTED_SHAPE.
  */
 fp8bs_status fp8bs_requant_T_128x1(fp8bs_requant_src src, const void *in, const float *s_in,
                                    int64_t T, int64_t C, int64_t ld_in, int64_t lds_in,

@@ -84,6 +84,7 @@ def grouped(a=A, sa=A, ldsa=2, b=A, sb=A, off=A, E=2, M=10, d=A, dt=0, N=128, K=
     (lambda: requant(lds_out=1), fp8bs.ERR_INVALID_ARG),
     (lambda: requant(q=A + 1), fp8bs.ERR_MISALIGNED),
     (lambda: requant(ld_out=264), fp8bs.ERR_MISALIGNED),
+    (lambda: requant(ld_in=1 << 25), fp8bs.ERR_UNSUPPORTED_SHAPE),
     (lambda: requant(T=0), fp8bs.OK),
     (lambda: gemm(bmode=2), fp8bs.ERR_INVALID_ARG),
     (lambda: gemm(dt=9), fp8bs.ERR_INVALID_ARG),
