@@ -610,35 +610,54 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // drain the clamped copies before exit
 
-  // ---- epilogue: lane holds columns n .. n+3 of row m per 16x16 block ----
-  const int fr = lane & 15;
-  const int kc = lane >> 4;
+  // ---- epilogue: the tile goes through LDS (padded rows) so that every
+  //      global store writes 16 contiguous bytes per lane and a wave writes
+  //      whole output rows.  Lane (fr, kc) holds columns 4 kc .. 4 kc + 3 of
+  //      row fr of each 16x16 block.
+  constexpr int OB = OUT_F32 ? 4 : 2;           // output bytes per element
+  constexpr int ROWB = BN * OB + 16;            // padded LDS row
+  constexpr int CPR = BN * OB / 16;             // 16-byte chunks per tile row
+  static_assert(BM * ROWB <= C::lds_bytes(BROW), "output tile fits the LDS");
+  block_barrier();  // every wave's copies have landed and its reads are done
+  {
+    const int fr = lane & 15;
+    const int kc = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < C::MB; ++i) {
-    const int64_t m = m0 + wm * (C::MB * 16) + i * 16 + fr;
-    if (m >= m_end) continue;
+    for (int i = 0; i < C::MB; ++i) {
+      const int r = wm * (C::MB * 16) + i * 16 + fr;
 #pragma unroll
-    for (int j = 0; j < C::NB; ++j) {
-      const int64_t n = n0 + wn * (C::NB * 16) + j * 16 + 4 * kc;
-      if (n >= p.N) continue;
-      const v4f v = acc[i][j];
-      if (OUT_F32) {
-        float* dst = static_cast<float*>(p.d) + m * p.ldd + n;
-        if (n + 3 < p.N) {
+      for (int j = 0; j < C::NB; ++j) {
+        const int c = wn * (C::NB * 16) + j * 16 + 4 * kc;
+        const v4f v = acc[i][j];
+        uint8_t* dst = lds + r * ROWB + c * OB;
+        if (OUT_F32) {
           *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
         } else {
-          for (int q = 0; q < 4 && n + q < p.N; ++q) dst[q] = v[q];
-        }
-      } else {
-        uint16_t* dst = static_cast<uint16_t*>(p.d) + m * p.ldd + n;
-        const uint32_t b0 = f32_to_bf16_rne(v[0]), b1 = f32_to_bf16_rne(v[1]);
-        const uint32_t b2 = f32_to_bf16_rne(v[2]), b3 = f32_to_bf16_rne(v[3]);
-        if (n + 3 < p.N) {
+          const uint32_t b0 = f32_to_bf16_rne(v[0]), b1 = f32_to_bf16_rne(v[1]);
+          const uint32_t b2 = f32_to_bf16_rne(v[2]), b3 = f32_to_bf16_rne(v[3]);
           *reinterpret_cast<uint2*>(dst) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-        } else {
-          const uint32_t bb[4] = {b0, b1, b2, b3};
-          for (int q = 0; q < 4 && n + q < p.N; ++q) dst[q] = static_cast<uint16_t>(bb[q]);
         }
+      }
+    }
+  }
+  __syncthreads();
+  {
+    uint8_t* dbase = static_cast<uint8_t*>(p.d);
+    const int64_t ldd_b = p.ldd * OB;
+    const int64_t cols = p.N - n0 < BN ? p.N - n0 : BN;   // valid columns of the tile
+#pragma unroll 4
+    for (int ch = tid; ch < BM * CPR; ch += C::NT) {
+      const int r = ch / CPR, cc = ch % CPR;
+      const int64_t m = m0 + r;
+      const int c0 = cc * (16 / OB);
+      if (m >= m_end || c0 >= cols) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + r * ROWB + cc * 16);
+      uint8_t* dst = dbase + m * ldd_b + (n0 + c0) * OB;
+      if (c0 + 16 / OB <= cols) {
+        *reinterpret_cast<uint4*>(dst) = v;
+      } else {
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(&v);
+        for (int e = 0; e < (cols - c0) * OB; ++e) dst[e] = src[e];
       }
     }
   }
