@@ -45,6 +45,9 @@
 //   of the tile order, and the order walks 4 M-tiles x all N-tiles per
 //   group, so the ~32 workgroups resident on one XCD share A and B panels
 //   in that XCD's L2.
+// * Workgroups are persistent (one per compute unit): after a tile's last
+//   K group the first K groups of the workgroup's next tile are copied while
+//   the finished tile goes out through LDS with 16-byte stores.
 #include <hip/hip_runtime.h>
 
 #include "fp8bs_device.h"
@@ -370,39 +373,43 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int G = static_cast<int>(p.K / 128);
 
-  // ---- tile ------------------------------------------------------------
-  int vm, nt;
-  tile_of(blockIdx.x, p.tiles_m, p.tiles_n, vm, nt);
-  const int64_t n0 = static_cast<int64_t>(nt) * BN;
-  int64_t m0, m_end;
+  // ---- tiles: the workgroup walks the virtual workgroup ids blockIdx.x,
+  //      blockIdx.x + gridDim.x, ... (gridDim.x is a multiple of the XCD
+  //      count, so every tile of a workgroup maps to the same XCD); the
+  //      first K groups of the next tile are copied while the current tile's
+  //      results are written out.
+  int64_t m0 = 0, m_end = 0, n0 = 0;
   const uint8_t* bmat = p.b;
   const float* sbmat = p.sb;
-  if (GROUPED) {
-    int64_t mt = vm;
-    int e = 0;
-    m0 = -1;
-    m_end = 0;
-    for (; e < p.E; ++e) {
-      // offsets are clamped into [0, M] so that inconsistent offsets can
-      // only give wrong rows, never an out-of-bounds access
-      int64_t r0 = p.offsets[e], r1 = p.offsets[e + 1];
-      r0 = r0 < 0 ? 0 : (r0 > p.M ? p.M : r0);
-      r1 = r1 < r0 ? r0 : (r1 > p.M ? p.M : r1);
-      const int64_t tiles = (r1 - r0 + BM - 1) / BM;
-      if (mt < tiles) {
-        m0 = r0 + mt * BM;
-        m_end = r1;
-        break;
+  const int vtiles = p.tiles_m * p.tiles_n;
+  auto plan_tile = [&](int v) -> bool {
+    int vm, nt;
+    tile_of(v, p.tiles_m, p.tiles_n, vm, nt);
+    n0 = static_cast<int64_t>(nt) * BN;
+    if (GROUPED) {
+      int64_t mt = vm;
+      for (int e = 0; e < p.E; ++e) {
+        // offsets are clamped into [0, M] so that inconsistent offsets can
+        // only give wrong rows, never an out-of-bounds access
+        int64_t r0 = p.offsets[e], r1 = p.offsets[e + 1];
+        r0 = r0 < 0 ? 0 : (r0 > p.M ? p.M : r0);
+        r1 = r1 < r0 ? r0 : (r1 > p.M ? p.M : r1);
+        const int64_t tiles = (r1 - r0 + BM - 1) / BM;
+        if (mt < tiles) {
+          m0 = r0 + mt * BM;
+          m_end = r1;
+          bmat = p.b + static_cast<int64_t>(e) * p.N * p.K;
+          sbmat = p.sb + static_cast<int64_t>(e) * ((p.N + 127) / 128) * G;
+          return true;
+        }
+        mt -= tiles;
       }
-      mt -= tiles;
+      return false;
     }
-    if (e == p.E || m0 < 0 || m0 >= m_end) return;  // uniform per workgroup
-    bmat = p.b + static_cast<int64_t>(e) * p.N * p.K;
-    sbmat = p.sb + static_cast<int64_t>(e) * ((p.N + 127) / 128) * G;
-  } else {
     m0 = static_cast<int64_t>(vm) * BM;
     m_end = p.M;
-  }
+    return true;
+  };
   // block mode: a wave's columns lie inside one 128-wide block of B
   static_assert(BROW || (128 % (C::NB * 16) == 0), "wave columns must not straddle a B block");
 
@@ -412,13 +419,10 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   //      or a B copy depends on q only, and its rows are the wave's rows of
   //      copy 0 moved by a multiple of 8 NW rows (a uniform offset).  Lane l
   //      fetches the global chunk (l & 7) ^ swizzle(row) of row l / 8 of its
-  //      copy; the swizzle does not depend on q.
+  //      copy; the swizzle does not depend on q.  The buffer descriptors
+  //      (per tile) cover the tile's valid rows.
   static_assert((BM / 8) % C::NW == 0 && C::NW % 2 == 0, "A copies must be whole rounds over the waves");
   constexpr int QA = BM / 8 / C::NW;  // copies per wave that move A rows
-  const int64_t rows_a = m_end - m0 < BM ? m_end - m0 : BM;
-  const int64_t rows_b = p.N - n0 < BN ? p.N - n0 : BN;
-  const i32x4 rs_a = make_rsrc(p.a + m0 * p.lda, static_cast<uint32_t>(rows_a * p.lda));
-  const i32x4 rs_b = make_rsrc(bmat + n0 * p.ldb, static_cast<uint32_t>(rows_b * p.ldb));
   const uint32_t lda = static_cast<uint32_t>(p.lda), ldb = static_cast<uint32_t>(p.ldb);
   uint32_t voff_a, voff_b;
   {
@@ -427,6 +431,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     voff_a = static_cast<uint32_t>(r) * lda + c * 16;
     voff_b = static_cast<uint32_t>(r) * ldb + c * 16;
   }
+  i32x4 rs_a, rs_b;
 
   // ---- scale copy plan: every issue copies one quarter of a scale block
   //      (SBLK groups).  The quarter is split into units of 16 rows x SBLK
@@ -443,9 +448,8 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     uint32_t voff, qstep, hstep, dst0, dstq, slot;
   };
   ScaleCopy sc[SPW];
+  const uint32_t ldsa4 = static_cast<uint32_t>(p.ldsa * 4), ldsb4 = static_cast<uint32_t>(p.ldsb * 4);
   {
-    const uint32_t ldsa4 = static_cast<uint32_t>(p.ldsa * 4), ldsb4 = static_cast<uint32_t>(p.ldsb * 4);
-    const i32x4 rs_sa = make_rsrc(p.sa + m0 * p.ldsa, static_cast<uint32_t>(rows_a) * ldsa4);
     const uint32_t gl = static_cast<uint32_t>(lane >> 4) * 4u;
 #pragma unroll
     for (int u = 0; u < SPW; ++u) {
@@ -454,7 +458,6 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
       x.hstep = SBLK * 4;
       x.slot = C::slot_bytes(BROW);
       if (c < SAW) {
-        x.rs = rs_sa;
         x.voff = static_cast<uint32_t>(16 * c + (lane & 15)) * ldsa4 + gl;
         x.qstep = 16 * SAW * ldsa4;
         x.dst0 = c * 256;
@@ -462,21 +465,17 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
       } else if (c < SAW + SBW) {
         const int w = c - SAW;
         if (BROW) {
-          x.rs = make_rsrc(sbmat + n0 * p.ldsb, static_cast<uint32_t>(rows_b) * ldsb4);
           x.voff = static_cast<uint32_t>(16 * w + (lane & 15)) * ldsb4 + gl;
           x.qstep = 16 * SBW * ldsb4;
           x.dst0 = C::SA_BYTES + w * 256;
           x.dstq = SBW * 256;
         } else {
-          const int64_t blocks = (rows_b + 127) / 128;
-          x.rs = make_rsrc(sbmat + (n0 / 128) * p.ldsb, static_cast<uint32_t>(blocks) * ldsb4);
           x.voff = static_cast<uint32_t>(lane & 15) * ldsb4 + gl;
           x.qstep = 0;
           x.dst0 = C::SA_BYTES;
           x.dstq = 0;
         }
       } else {
-        x.rs = rs_sa;
         x.voff = 0;
         x.qstep = 0;
         x.hstep = 0;
@@ -486,6 +485,28 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
       }
     }
   }
+  // per-tile descriptors
+  auto set_descriptors = [&]() {
+    const int64_t rows_a = m_end - m0 < BM ? m_end - m0 : BM;
+    const int64_t rows_b = p.N - n0 < BN ? p.N - n0 : BN;
+    rs_a = make_rsrc(p.a + m0 * p.lda, static_cast<uint32_t>(rows_a * p.lda));
+    rs_b = make_rsrc(bmat + n0 * p.ldb, static_cast<uint32_t>(rows_b * p.ldb));
+    const i32x4 rs_sa = make_rsrc(p.sa + m0 * p.ldsa, static_cast<uint32_t>(rows_a) * ldsa4);
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+      const int c = wave + u * C::NW;
+      if (c >= SAW && c < SAW + SBW) {
+        if (BROW) {
+          sc[u].rs = make_rsrc(sbmat + n0 * p.ldsb, static_cast<uint32_t>(rows_b) * ldsb4);
+        } else {
+          const int64_t blocks = (rows_b + 127) / 128;
+          sc[u].rs = make_rsrc(sbmat + (n0 / 128) * p.ldsb, static_cast<uint32_t>(blocks) * ldsb4);
+        }
+      } else {
+        sc[u].rs = rs_sa;
+      }
+    }
+  };
 
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&lds[0]));
   constexpr int COPIES = C::DPW + SPW;  // vector-memory ops per wave per issue
@@ -498,8 +519,8 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     copy4_to_lds(x.rs, x.voff, x.qstep * q + x.hstep * h, dst);
   };
   // part k of issue t: tile copy k (k < DPW) of K group min(t, G - 1) into
-  // `stage`, or (k == DPW) quarter t % 4 of scale block t / 4 + 1 (block 0
-  // is copied up front)
+  // `stage`, or (k >= DPW) copy k - DPW of quarter t % 4 of scale block
+  // t / 4 + 1 (block 0 is copied with the first two issues)
   auto issue_part = [&](int t, int stage, int k) {
     const uint32_t gk = static_cast<uint32_t>(t < G - 1 ? t : G - 1) * 128u;
     const uint32_t base = lds_base + stage * C::STAGE;
@@ -511,37 +532,37 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     else
       issue_scales(k - C::DPW, t & 3, (t >> 2) + 1);
   };
-  // issue t: the tile rows of K group min(t, G - 1) into `stage`, and
-  // quarter t % 4 of scale block t / 4 + 1 (block 0 is copied up front)
   auto issue = [&](int t, int stage) {
-    const uint32_t gk = static_cast<uint32_t>(t < G - 1 ? t : G - 1) * 128u;
-    const uint32_t base = lds_base + stage * C::STAGE;
 #pragma unroll
-    for (int q = 0; q < C::DPW; ++q) {
-      if (q < QA)
-        copy16_to_lds(rs_a, voff_a, gk + q * (8 * C::NW) * lda, base + (q * C::NW + wave) * 1024);
-      else
-        copy16_to_lds(rs_b, voff_b, gk + (q - QA) * (8 * C::NW) * ldb,
-                      base + C::A_BYTES + ((q - QA) * C::NW + wave) * 1024);
-    }
+    for (int k = 0; k < COPIES; ++k) issue_part(t, stage, k);
+  };
+  // the copies a tile needs before its first barrier: scale block 0 and
+  // issues 0 and 1
+  auto issue_head = [&]() {
 #pragma unroll
-    for (int u = 0; u < SPW; ++u) issue_scales(u, t & 3, (t >> 2) + 1);
+    for (int q = 0; q < SBLK; ++q)
+#pragma unroll
+      for (int u = 0; u < SPW; ++u) issue_scales(u, q, 0);
+    issue(0, 0);
+    issue(1, 1);
   };
   auto slot_of = [&](int g) {
     return reinterpret_cast<const float*>(lds + C::sc_area() + ((g / SBLK) % NSLOT) * SLOT);
   };
 
-  v4f acc[C::MB][C::NB];
-#pragma unroll
-  for (int i = 0; i < C::MB; ++i)
-#pragma unroll
-    for (int j = 0; j < C::NB; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  int v = blockIdx.x;
+  while (v < vtiles && !plan_tile(v)) v += gridDim.x;
+  if (v >= vtiles) return;  // uniform per workgroup
+  set_descriptors();
+  issue_head();
 
+  for (;;) {
+    v4f acc[C::MB][C::NB];
 #pragma unroll
-  for (int q = 0; q < SBLK; ++q)
+    for (int i = 0; i < C::MB; ++i)
 #pragma unroll
-    for (int u = 0; u < SPW; ++u) issue_scales(u, q, 0);
-  if constexpr (C::NSTAGE == 3) {
+      for (int j = 0; j < C::NB; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
     // Pipeline over three stages, stage(x) = x % 3.  Before iteration g:
     // fragments of group g are in registers (cur), stage(g + 1) holds group
     // g + 1 and is visible, the copy of group g + 2 into stage(g + 2) is in
@@ -553,9 +574,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     // 4h - 1, and its slot was last read in iteration 4h - 10.  Copies and
     // reads past the last group are clamped to valid data that is never
     // used.
-    issue(0, 0);
-    issue(1, 1);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this tile's head copies (and earlier stores)
     block_barrier();
     Frag<C> f0, f1;
     load_frag<C, BROW>(f0, lds, slot_of(0), 0, wm, wn, lane);
@@ -589,77 +608,78 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     }
     if (g < G)  // odd G: the last group's fragments are in f0
       compute<C, BROW>(acc, f0);
-  } else {
-    // Two stages, stage(x) = x % 2.  Iteration g starts issue g + 1 into
-    // the other stage (read during iteration g - 1, finished before the last
-    // barrier), multiplies g straight from LDS, then waits for the copies
-    // and its own reads before the barrier.  Scale block h is copied by
-    // issues 4h - 4 .. 4h - 1 (iterations 4h - 5 .. 4h - 2) and first read
-    // in iteration 4h.
-    issue(0, 0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    block_barrier();
-    for (int g = 0; g < G; ++g) {
-      const int st = g & 1;
-      issue(g + 1, st ^ 1);
-      compute_lds<C, BROW>(acc, lds + st * C::STAGE, slot_of(g), g & 3, wm, wn, lane);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
-      block_barrier();
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // drain the clamped copies before exit
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the clamped copies past the last group
+    block_barrier();                            // every stage and scale slot is free
 
-  // ---- epilogue: the tile goes through LDS (padded rows) so that every
-  //      global store writes 16 contiguous bytes per lane and a wave writes
-  //      whole output rows.  Lane (fr, kc) holds columns 4 kc .. 4 kc + 3 of
-  //      row fr of each 16x16 block.
-  constexpr int OB = OUT_F32 ? 4 : 2;           // output bytes per element
-  constexpr int ROWB = BN * OB + 16;            // padded LDS row
-  constexpr int CPR = BN * OB / 16;             // 16-byte chunks per tile row
-  static_assert(BM * ROWB <= C::lds_bytes(BROW), "output tile fits the LDS");
-  block_barrier();  // every wave's copies have landed and its reads are done
-  {
-    const int fr = lane & 15;
-    const int kc = lane >> 4;
+    // ---- next tile: its head copies go out before this tile's results
+    const int64_t cm0 = m0, cm_end = m_end, cn0 = n0;
+    v += gridDim.x;
+    while (v < vtiles && !plan_tile(v)) v += gridDim.x;
+    const bool more = v < vtiles;
+    if (more) {
+      set_descriptors();
+      issue_head();
+    }
+
+    // ---- epilogue through stage 2 of the LDS (padded rows, PR rows per
+    //      pass), so that every global store writes 16 contiguous bytes per
+    //      lane and a wave writes whole output rows.  Lane (fr, kc) holds
+    //      columns 4 kc .. 4 kc + 3 of row fr of each 16x16 block.
+    constexpr int OB = OUT_F32 ? 4 : 2;           // output bytes per element
+    constexpr int ROWB = BN * OB + 16;            // padded LDS row
+    constexpr int CPR = BN * OB / 16;             // 16-byte chunks per tile row
+    constexpr int PR0 = C::STAGE / ROWB;          // rows that fit one stage
+    constexpr int PR = PR0 >= BM ? BM : PR0 >= 128 ? 128 : PR0 >= 64 ? 64 : PR0 >= 32 ? 32 : 16;
+    static_assert(PR <= PR0 && BM % PR == 0, "output passes");
+    uint8_t* const ob = lds + 2 * C::STAGE;
+    uint8_t* dbase = static_cast<uint8_t*>(p.d);
+    const int64_t ldd_b = p.ldd * OB;
+    const int64_t cols = p.N - cn0 < BN ? p.N - cn0 : BN;   // valid columns of the tile
 #pragma unroll
-    for (int i = 0; i < C::MB; ++i) {
-      const int r = wm * (C::MB * 16) + i * 16 + fr;
+    for (int pass = 0; pass < BM / PR; ++pass) {
+      if (pass > 0) block_barrier();  // previous pass read out of the LDS
+      {
+        const int fr = lane & 15;
+        const int kc = lane >> 4;
 #pragma unroll
-      for (int j = 0; j < C::NB; ++j) {
-        const int c = wn * (C::NB * 16) + j * 16 + 4 * kc;
-        const v4f v = acc[i][j];
-        uint8_t* dst = lds + r * ROWB + c * OB;
-        if (OUT_F32) {
-          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        for (int i = 0; i < C::MB; ++i) {
+          const int rb = wm * (C::MB * 16) + i * 16;  // first row of the block
+          if (rb / PR != pass) continue;              // uniform
+          const int r = rb % PR + fr;
+#pragma unroll
+          for (int j = 0; j < C::NB; ++j) {
+            const int c = wn * (C::NB * 16) + j * 16 + 4 * kc;
+            const v4f vv = acc[i][j];
+            uint8_t* dst = ob + r * ROWB + c * OB;
+            if (OUT_F32) {
+              *reinterpret_cast<float4*>(dst) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+            } else {
+              const uint32_t b0 = f32_to_bf16_rne(vv[0]), b1 = f32_to_bf16_rne(vv[1]);
+              const uint32_t b2 = f32_to_bf16_rne(vv[2]), b3 = f32_to_bf16_rne(vv[3]);
+              *reinterpret_cast<uint2*>(dst) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);  // this wave's LDS writes are done
+      block_barrier();
+#pragma unroll 4
+      for (int ch = tid; ch < PR * CPR; ch += C::NT) {
+        const int r = ch / CPR, cc = ch % CPR;
+        const int64_t m = cm0 + pass * PR + r;
+        const int c0 = cc * (16 / OB);
+        if (m >= cm_end || c0 >= cols) continue;
+        const uint4 vv = *reinterpret_cast<const uint4*>(ob + r * ROWB + cc * 16);
+        uint8_t* dst = dbase + m * ldd_b + (cn0 + c0) * OB;
+        if (c0 + 16 / OB <= cols) {
+          *reinterpret_cast<uint4*>(dst) = vv;
         } else {
-          const uint32_t b0 = f32_to_bf16_rne(v[0]), b1 = f32_to_bf16_rne(v[1]);
-          const uint32_t b2 = f32_to_bf16_rne(v[2]), b3 = f32_to_bf16_rne(v[3]);
-          *reinterpret_cast<uint2*>(dst) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+          const uint8_t* src = reinterpret_cast<const uint8_t*>(&vv);
+          for (int e = 0; e < (cols - c0) * OB; ++e) dst[e] = src[e];
         }
       }
     }
-  }
-  __syncthreads();
-  {
-    uint8_t* dbase = static_cast<uint8_t*>(p.d);
-    const int64_t ldd_b = p.ldd * OB;
-    const int64_t cols = p.N - n0 < BN ? p.N - n0 : BN;   // valid columns of the tile
-#pragma unroll 4
-    for (int ch = tid; ch < BM * CPR; ch += C::NT) {
-      const int r = ch / CPR, cc = ch % CPR;
-      const int64_t m = m0 + r;
-      const int c0 = cc * (16 / OB);
-      if (m >= m_end || c0 >= cols) continue;
-      const uint4 v = *reinterpret_cast<const uint4*>(lds + r * ROWB + cc * 16);
-      uint8_t* dst = dbase + m * ldd_b + (n0 + c0) * OB;
-      if (c0 + 16 / OB <= cols) {
-        *reinterpret_cast<uint4*>(dst) = v;
-      } else {
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(&v);
-        for (int e = 0; e < (cols - c0) * OB; ++e) dst[e] = src[e];
-      }
-    }
+    if (!more) break;
   }
 }
 
@@ -669,7 +689,10 @@ hipError_t dispatch(GemmArgs args, int64_t tiles_m_extra, bool out_f32, hipStrea
   if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
   args.tiles_m = static_cast<int32_t>(tm);
   args.tiles_n = static_cast<int32_t>(tn);
-  const dim3 grid(static_cast<unsigned>(tm * tn)), block(C::NT);
+  // persistent: one workgroup per compute unit of a 256-CU MI355X (a
+  // multiple of the XCD count), each walking tiles gridDim.x apart
+  const int64_t vt = tm * tn;
+  const dim3 grid(static_cast<unsigned>(vt < 256 ? vt : 256)), block(C::NT);
   if (out_f32) hipLaunchKernelGGL((gemm_kernel<C, true, BROW, GROUPED>), grid, block, 0, st, args);
   else hipLaunchKernelGGL((gemm_kernel<C, false, BROW, GROUPED>), grid, block, 0, st, args);
   return hipGetLastError();
