@@ -128,13 +128,13 @@ def cpu_baseline(x_u16, w_u16, M, N, K):
     oracle.build(force=False)
     threads = oracle.num_threads()
     t0 = time.perf_counter()
-    qa_rows = 256
+    qa_rows = 1024
     qa, sa = oracle.quant_act_1x128(x_u16[:qa_rows])
     t_qa = time.perf_counter() - t0
     t0 = time.perf_counter()
     qb, sb = oracle.quant_w_128x128(w_u16)
     t_qw = time.perf_counter() - t0
-    g_rows = min(64, max(8, 2 * threads))
+    g_rows = min(128, max(16, 6 * threads))
     t0 = time.perf_counter()
     oracle.gemm(qa[:g_rows], sa[:g_rows], qb, sb)
     t_g = time.perf_counter() - t0
