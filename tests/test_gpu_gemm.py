@@ -99,6 +99,21 @@ def test_gemm_ragged_strided(M, N, K):
     _full_check(f"ragged-row {M}x{N}x{K}", qa, sa, qbr, sbr, oracle.BSCALE_ROW, pads=(0, 0, 0, 2, 0))
 
 
+def test_gemm_many_ragged_tiles():
+    """More tiles than workgroups (each workgroup walks several tiles, the
+    next tile's first copies overlapping the previous tile's output), with
+    ragged M and N in both B-scale modes."""
+    native_loaded()
+    M, N, K = 1000, 9000, 384
+    q = synth.tiny(M=M, N=N, K=K, seed=5)
+    qa, sa = oracle.quant_act_1x128(q["A"])
+    qb, sb = oracle.quant_w_128x128(q["W"])
+    announce(f"gemm many tiles {M}x{N}x{K}")
+    _full_check(f"many-tiles {M}x{N}x{K}", qa, sa, qb, sb)
+    qbr, sbr = oracle.quant_act_1x128(q["W"])
+    _full_check(f"many-tiles-row {M}x{N}x{K}", qa, sa, qbr, sbr, oracle.BSCALE_ROW)
+
+
 def test_gemm_edge_scales_and_codes():
     """Zero, subnormal and huge scales; saturated codes; negative zeros."""
     native_loaded()
