@@ -151,6 +151,22 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   nt = rr / gm;
 }
 
+// Copies for the GEMM loop: M0 is set without being saved or restored.  The
+// compiler never uses M0 in this file's kernels (tests/test_gemm_m0.py checks
+// the generated code), so nothing it relies on is disturbed.
+__device__ __forceinline__ void gemm_copy16(const i32x4& rsrc, uint32_t voff, uint32_t soff,
+                                            uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);  // uniform by contract
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+__device__ __forceinline__ void gemm_copy4(const i32x4& rsrc, uint32_t voff, uint32_t soff,
+                                           uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);  // uniform by contract
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
 // Fragments (and their scales) of one K group for one wave.
 template <class C>
 struct Frag {
@@ -424,12 +440,14 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   static_assert((BM / 8) % C::NW == 0 && C::NW % 2 == 0, "A copies must be whole rounds over the waves");
   constexpr int QA = BM / 8 / C::NW;  // copies per wave that move A rows
   const uint32_t lda = static_cast<uint32_t>(p.lda), ldb = static_cast<uint32_t>(p.ldb);
-  uint32_t voff_a, voff_b;
+  uint32_t voff[C::DPW];  // copy k: its rows' offsets from the tile's first row
   {
     const int r = 8 * wave + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
-    voff_a = static_cast<uint32_t>(r) * lda + c * 16;
-    voff_b = static_cast<uint32_t>(r) * ldb + c * 16;
+#pragma unroll
+    for (int k = 0; k < C::DPW; ++k)
+      voff[k] = k < QA ? static_cast<uint32_t>(r + k * 8 * C::NW) * lda + c * 16
+                       : static_cast<uint32_t>(r + (k - QA) * 8 * C::NW) * ldb + c * 16;
   }
   i32x4 rs_a, rs_b;
 
@@ -516,7 +534,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   auto issue_scales = [&](int u, int q, int h) {
     const ScaleCopy& x = sc[u];
     const uint32_t dst = lds_base + C::sc_area() + (h % NSLOT) * x.slot + x.dst0 + x.dstq * q;
-    copy4_to_lds(x.rs, x.voff, x.qstep * q + x.hstep * h, dst);
+    gemm_copy4(x.rs, x.voff, x.qstep * q + x.hstep * h, dst);
   };
   // part k of issue t: tile copy k (k < DPW) of K group min(t, G - 1) into
   // `stage`, or (k >= DPW) copy k - DPW of quarter t % 4 of scale block
@@ -525,10 +543,9 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     const uint32_t gk = static_cast<uint32_t>(t < G - 1 ? t : G - 1) * 128u;
     const uint32_t base = lds_base + stage * C::STAGE;
     if (k < QA)
-      copy16_to_lds(rs_a, voff_a, gk + k * (8 * C::NW) * lda, base + (k * C::NW + wave) * 1024);
+      gemm_copy16(rs_a, voff[k], gk, base + (k * C::NW + wave) * 1024);
     else if (k < C::DPW)
-      copy16_to_lds(rs_b, voff_b, gk + (k - QA) * (8 * C::NW) * ldb,
-                    base + C::A_BYTES + ((k - QA) * C::NW + wave) * 1024);
+      gemm_copy16(rs_b, voff[k], gk, base + C::A_BYTES + ((k - QA) * C::NW + wave) * 1024);
     else
       issue_scales(k - C::DPW, t & 3, (t >> 2) + 1);
   };
