@@ -62,7 +62,7 @@ typedef __attribute__((ext_vector_type(4))) float v4f;
 constexpr int GROUP_M = 4;     // M-tiles per group of the tile order
 constexpr int NUM_XCD = 8;
 constexpr int SBLK = 4;        // K groups per scale block
-constexpr int NSLOT = 3;       // scale blocks resident in LDS
+constexpr int NSLOT = 4;       // scale blocks resident in LDS (a power of two: cheap slot index)
 
 // Workgroup tile BM x BN, WM x WN waves of (BM/WM) x (BN/WN).
 // NSTAGE = 3: fragments of the next K group are read from LDS while the
@@ -588,7 +588,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     // multiplies g, then waits for issue g + 2 and for its own LDS reads
     // before the barrier.  Scale block h is copied by issues 4h - 4 ..
     // 4h - 1 (iterations 4h - 7 .. 4h - 4), is first read in iteration
-    // 4h - 1, and its slot was last read in iteration 4h - 10.  Copies and
+    // 4h - 1, and its slot (NSLOT = 4) was last read in iteration 4h - 14.  Copies and
     // reads past the last group are clamped to valid data that is never
     // used.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this tile's head copies (and earlier stores)
