@@ -62,7 +62,7 @@ typedef __attribute__((ext_vector_type(4))) float v4f;
 constexpr int GROUP_M = 4;     // M-tiles per group of the tile order
 constexpr int NUM_XCD = 8;
 constexpr int SBLK = 4;        // K groups per scale block
-constexpr int NSLOT = 4;       // scale blocks resident in LDS (a power of two: cheap slot index)
+constexpr int NSLOT = 3;       // scale blocks resident in LDS
 
 // Workgroup tile BM x BN, WM x WN waves of (BM/WM) x (BN/WN).
 // NSTAGE = 3: fragments of the next K group are read from LDS while the
@@ -531,9 +531,10 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   constexpr int SLOT = C::slot_bytes(BROW);
 
   // this wave's copy u of quarter q of scale block h
-  auto issue_scales = [&](int u, int q, int h) {
+  // (hs = h % NSLOT, passed separately so that it can be a constant)
+  auto issue_scales = [&](int u, int q, int h, int hs) {
     const ScaleCopy& x = sc[u];
-    const uint32_t dst = lds_base + C::sc_area() + (h % NSLOT) * x.slot + x.dst0 + x.dstq * q;
+    const uint32_t dst = lds_base + C::sc_area() + hs * x.slot + x.dst0 + x.dstq * q;
     gemm_copy4(x.rs, x.voff, x.qstep * q + x.hstep * h, dst);
   };
   // part k of issue t: tile copy k (k < DPW) of K group min(t, G - 1) into
@@ -547,7 +548,19 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     else if (k < C::DPW)
       gemm_copy16(rs_b, voff[k], gk, base + C::A_BYTES + ((k - QA) * C::NW + wave) * 1024);
     else
-      issue_scales(k - C::DPW, t & 3, (t >> 2) + 1);
+      issue_scales(k - C::DPW, t & 3, (t >> 2) + 1, ((t >> 2) + 1) % NSLOT);
+  };
+  // the same with the issue's quarter and scale slot given (constants in
+  // the unrolled loop)
+  auto issue_part_q = [&](int t, int stage, int q, int h, int hs, int k) {
+    const uint32_t gk = static_cast<uint32_t>(t < G - 1 ? t : G - 1) * 128u;
+    const uint32_t base = lds_base + stage * C::STAGE;
+    if (k < QA)
+      gemm_copy16(rs_a, voff[k], gk, base + (k * C::NW + wave) * 1024);
+    else if (k < C::DPW)
+      gemm_copy16(rs_b, voff[k], gk, base + C::A_BYTES + ((k - QA) * C::NW + wave) * 1024);
+    else
+      issue_scales(k - C::DPW, q, h, hs);
   };
   auto issue = [&](int t, int stage) {
 #pragma unroll
@@ -559,7 +572,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int q = 0; q < SBLK; ++q)
 #pragma unroll
-      for (int u = 0; u < SPW; ++u) issue_scales(u, q, 0);
+      for (int u = 0; u < SPW; ++u) issue_scales(u, q, 0, 0);
     issue(0, 0);
     issue(1, 1);
   };
@@ -599,32 +612,32 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     issue(2, 2);
     block_barrier();
 
-    int g = 0;
-    int st1 = 1;  // stage(g + 1)
-    for (; g + 2 <= G; g += 2) {
-      // iteration g: cur = f0, next = f1
-      {
-        const int t = g + 3, st = st1 == 0 ? 2 : st1 - 1;
-        pipelined_group<C, BROW, COPIES>(acc, f0, f1, lds + st1 * C::STAGE, slot_of(g + 1), (g + 1) & 3,
-                                         wm, wn, lane, [&](int k) { issue_part(t, st, k); });
+    // Unrolled by 12 (fragment sets alternate with period 2, stages with 3,
+    // scale quarters with 4, scale slots with 12) so that every stage, slot
+    // and quarter index is a constant; iteration g + i runs only if
+    // g + i < G.  The last iteration reads fragments of the (clamped)
+    // group G, which are never used.
+    for (int g = 0; g < G; g += 12) {
+      const int hb = g / 4;  // scale blocks before this round
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        if (g + i < G) {
+          Frag<C>& cur = (i & 1) ? f1 : f0;
+          Frag<C>& nxt = (i & 1) ? f0 : f1;
+          const int t = g + i + 3;                   // this iteration's issue
+          const int q = (i + 3) & 3;                 // its scale quarter
+          const int hl = (i + 3) / 4 + 1;            // its scale block, minus hb
+          const float* slot_n = reinterpret_cast<const float*>(
+              lds + C::sc_area() + (((i + 1) / 4) % NSLOT) * SLOT);  // group g + i + 1 (hb % 3 == 0)
+          pipelined_group<C, BROW, COPIES>(
+              acc, cur, nxt, lds + ((i + 1) % 3) * C::STAGE, slot_n, (i + 1) & 3, wm, wn, lane,
+              [&](int k) { issue_part_q(t, i % 3, q, hb + hl, hl % NSLOT, k); });
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(COPIES));
+          __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+          block_barrier();
+        }
       }
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(COPIES));
-      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
-      block_barrier();
-      st1 = st1 == 2 ? 0 : st1 + 1;
-      // iteration g + 1: cur = f1, next = f0
-      {
-        const int t = g + 4, st = st1 == 0 ? 2 : st1 - 1;
-        pipelined_group<C, BROW, COPIES>(acc, f1, f0, lds + st1 * C::STAGE, slot_of(g + 2), (g + 2) & 3,
-                                         wm, wn, lane, [&](int k) { issue_part(t, st, k); });
-      }
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(COPIES));
-      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
-      block_barrier();
-      st1 = st1 == 2 ? 0 : st1 + 1;
     }
-    if (g < G)  // odd G: the last group's fragments are in f0
-      compute<C, BROW>(acc, f0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the clamped copies past the last group
     block_barrier();                            // every stage and scale slot is free
 
