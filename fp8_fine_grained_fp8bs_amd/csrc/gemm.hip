@@ -601,9 +601,9 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     // multiplies g, then waits for issue g + 2 and for its own LDS reads
     // before the barrier.  Scale block h is copied by issues 4h - 4 ..
     // 4h - 1 (iterations 4h - 7 .. 4h - 4), is first read in iteration
-    // 4h - 1, and its slot (NSLOT = 4) was last read in iteration 4h - 14.  Copies and
-    // reads past the last group are clamped to valid data that is never
-    // used.
+    // 4h - 1, and its slot (NSLOT = 3) was last read in iteration
+    // 4h - 10.  Copies and reads past the last group are clamped to valid
+    // data that is never used.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this tile's head copies (and earlier stores)
     block_barrier();
     Frag<C> f0, f1;
