@@ -148,7 +148,8 @@ def cpu_baseline(x_u16, w_u16, M, N, K):
 
 
 def time_rows(dev, reps=20, warm=3):
-    """Re-quantization, wgrad GEMM and grouped GEMM rows, at their full sizes."""
+    """Re-quantization, wgrad GEMM, weight transpose and input-gradient GEMM, and
+    grouped GEMM rows, at their full sizes."""
     import numpy as np
     import torch
     from fp8_fine_grained_fp8bs_amd import fp8bs, synth
@@ -165,7 +166,7 @@ def time_rows(dev, reps=20, warm=3):
 
     # backward wgrad: X 8192x7168, dY 8192x2048
     log("rows: wgrad inputs")
-    w = synth.wgrad()
+    w = synth.wgrad(with_w=True)
     T, C_in = w["X"].shape
     C_out = w["dY"].shape[1]
     X = bf16_dev(w["X"], dev)
@@ -190,7 +191,26 @@ def time_rows(dev, reps=20, warm=3):
     fl = 2.0 * C_in * C_out * T
     rows["gemm_wgrad_row_f32"] = {"shape": f"M{C_in} N{C_out} K{T}", "us": ms * 1e3,
                                   "TFLOP/s": fl / ms / 1e9, "frac_fp8_peak": fl / ms / 1e9 / FP8_PEAK_TFLOPS}
-    del X, dY, qx, sx, qxt, sxt, qdt, sdt, dW, w
+
+    # backward for the input: dX [T][C_in] = dY W, W [C_out][C_in] quantized in
+    # 128x128 blocks and transposed for the K-contiguous GEMM
+    log("rows: input-gradient inputs")
+    Wd = bf16_dev(w["W"], dev)
+    qdy, sdy = fp8bs.quant_act_1x128(dY)
+    qw, sw = fp8bs.quant_w_128x128(Wd)
+    qwt = torch.empty((C_in, C_out), dtype=torch.uint8, device=dev)
+    swt = torch.empty((C_in // 128, C_out // 128), dtype=torch.float32, device=dev)
+    dX = torch.empty((T, C_in), dtype=torch.bfloat16, device=dev)
+    ms = timed("transpose_w", lambda: fp8bs.fp8bs_transpose_w_128x128(qw, sw, qwt, swt))
+    b = C_out * C_in * 2 + 2 * (C_out // 128) * (C_in // 128) * 4
+    rows["transpose_w_128x128"] = {"shape": f"[{C_out}][{C_in}] -> [{C_in}][{C_out}]", "us": ms * 1e3,
+                                   "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / HBM_PEAK_GBS,
+                                   "bytes": b}
+    ms = timed("dgrad", lambda: fp8bs.fp8bs_gemm(qdy, sdy, qwt, swt, fp8bs.BSCALE_BLOCK_128x128, dX, fp8bs.OUT_BF16))
+    fl = 2.0 * T * C_in * C_out
+    rows["gemm_dgrad_bf16"] = {"shape": f"M{T} N{C_in} K{C_out}", "us": ms * 1e3,
+                               "TFLOP/s": fl / ms / 1e9, "frac_fp8_peak": fl / ms / 1e9 / FP8_PEAK_TFLOPS}
+    del X, dY, qx, sx, qxt, sxt, qdt, sdt, dW, w, Wd, qdy, sdy, qw, sw, qwt, swt, dX
 
     # grouped MoE (8 experts, 16384 tokens, Zipf counts)
     log("rows: moe inputs")

@@ -21,7 +21,7 @@ std::atomic<int> g_dev_state[kMaxDevices];
 // 4 GiB, so that 32-bit offsets from its first row reach every element.
 constexpr int64_t kMaxCodeStride = int64_t(1) << 24;   // bytes per code row
 constexpr int64_t kMaxScaleStride = int64_t(1) << 22;  // floats per scale row
-constexpr int64_t kMaxRequantStride = int64_t(1) << 25;  // bytes per input row of requant
+constexpr int64_t kMaxRequantStride = int64_t(1) << 25;  // bytes per input row: requant, transpose
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -139,6 +139,23 @@ fp8bs_status fp8bs_requant_T_128x1(fp8bs_requant_src src, const void* in, const 
   FP8BS_TRY(check_device());
   return launched(fp8bs::launch_requant_T_128x1(bf16, in, s_in, T, C, ld_in, lds_in, q_out, ld_out,
                                                 s_out, lds_out, static_cast<hipStream_t>(stream)));
+}
+
+fp8bs_status fp8bs_transpose_w_128x128(const uint8_t* q, int64_t N, int64_t K, int64_t ldq,
+                                       const float* s, int64_t lds, uint8_t* qt, int64_t ldqt,
+                                       float* st, int64_t ldst, void* stream) {
+  if (N < 0 || K <= 0) return FP8BS_ERR_INVALID_ARG;
+  if (N % 128 != 0 || K % 128 != 0) return FP8BS_ERR_UNSUPPORTED_SHAPE;
+  if (N == 0) return FP8BS_OK;
+  FP8BS_TRY(check_matrix(q, K, ldq, 1));
+  FP8BS_TRY(check_scales(s, K / 128, lds));
+  FP8BS_TRY(check_matrix(qt, N, ldqt, 1));
+  FP8BS_TRY(check_scales(st, N / 128, ldst));
+  // 128-row blocks are addressed with 32-bit offsets from their first row
+  if (ldq >= kMaxRequantStride) return FP8BS_ERR_UNSUPPORTED_SHAPE;
+  FP8BS_TRY(check_device());
+  return launched(fp8bs::launch_transpose_w_128x128(q, N, K, ldq, s, lds, qt, ldqt, st, ldst,
+                                                    static_cast<hipStream_t>(stream)));
 }
 
 fp8bs_status fp8bs_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa,

@@ -147,10 +147,13 @@ __device__ __forceinline__ float wave_max(float v) {
   return __int_as_float(x);
 }
 
-// bf16 from float, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// Two floats to two bf16 (low half = a), round to nearest even: one
+// v_cvt_pk_bf16_f32 (IEEE rounding of the default mode; FP32 subnormals
+// kept).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
 }
 
 // Direct global -> LDS copies through buffer descriptors.

@@ -19,6 +19,10 @@ hipError_t launch_requant_T_128x1(bool src_bf16, const void* in, const float* s_
                                   uint8_t* q_out, int64_t ld_out, float* s_out,
                                   int64_t lds_out, hipStream_t st);
 
+hipError_t launch_transpose_w_128x128(const uint8_t* q, int64_t N, int64_t K, int64_t ldq,
+                                      const float* s, int64_t lds, uint8_t* qt, int64_t ldqt,
+                                      float* st, int64_t ldst, hipStream_t stream);
+
 hipError_t launch_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa,
                        const uint8_t* b, const float* sb, int64_t ldb, int64_t ldsb,
                        bool bscale_row, void* d, int64_t ldd, bool out_f32,

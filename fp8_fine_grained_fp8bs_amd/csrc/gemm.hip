@@ -684,9 +684,8 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
             if (OUT_F32) {
               *reinterpret_cast<float4*>(dst) = make_float4(vv[0], vv[1], vv[2], vv[3]);
             } else {
-              const uint32_t b0 = f32_to_bf16_rne(vv[0]), b1 = f32_to_bf16_rne(vv[1]);
-              const uint32_t b2 = f32_to_bf16_rne(vv[2]), b3 = f32_to_bf16_rne(vv[3]);
-              *reinterpret_cast<uint2*>(dst) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+              *reinterpret_cast<uint2*>(dst) =
+                  make_uint2(pack_bf16x2_rne(vv[0], vv[1]), pack_bf16x2_rne(vv[2], vv[3]));
             }
           }
         }

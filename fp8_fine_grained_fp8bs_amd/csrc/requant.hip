@@ -9,7 +9,8 @@
 // token dimension becomes the contiguous K of the weight-gradient GEMM.
 //
 // The tile goes through LDS once, so every input and output byte crosses
-// HBM once.
+// HBM once.  The same tile machinery transposes 128x128-block-quantized
+// weights for the backward pass for the input (transpose_w_kernel).
 #include <hip/hip_runtime.h>
 
 #include "fp8bs_device.h"
@@ -145,6 +146,99 @@ __global__ __launch_bounds__(256) void requant_kernel(const uint8_t* __restrict_
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
+// ---------------------------------------------------------------------
+// Transpose of 128x128-block-quantized weights, for the backward pass for
+// the input ([p3] para 4 splits the backward pass into a part for the
+// input and a part for the weights).  dX = dY W consumes W as the B
+// operand of a K-contiguous GEMM, i.e. as W^T [K][N].  The max-abs of a
+// 128x128 block does not depend on its orientation, so the blocks of W^T
+// are the transposed blocks of W with the same scales: the codes move as
+// bytes and the scale grid is transposed; nothing is re-quantized.
+//
+// A tile is one 128x128 block.  The copy plan and the LDS swizzle are
+// those of requant_kernel (rows are the N index, 128 code bytes each);
+// each thread reads 16 consecutive rows of one dword column (4 k), turns
+// the 16x4 bytes around with byte permutes, and writes 16 bytes to each
+// of its 4 output rows.
+// ---------------------------------------------------------------------
+// transpose of a 4x4 byte block: byte c of result[c'] = byte c' of w[c]
+__device__ __forceinline__ void transpose4x4(const uint32_t (&w)[4], uint32_t (&t)[4]) {
+  const uint32_t x0 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // w0.b0 w1.b0 w0.b1 w1.b1
+  const uint32_t x1 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // w0.b2 w1.b2 w0.b3 w1.b3
+  const uint32_t y0 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+  const uint32_t y1 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+  t[0] = __builtin_amdgcn_perm(y0, x0, 0x05040100u);
+  t[1] = __builtin_amdgcn_perm(y0, x0, 0x07060302u);
+  t[2] = __builtin_amdgcn_perm(y1, x1, 0x05040100u);
+  t[3] = __builtin_amdgcn_perm(y1, x1, 0x07060302u);
+}
+
+__global__ __launch_bounds__(256) void transpose_w_kernel(const uint8_t* __restrict__ q, int64_t ldq,
+                                                          const float* __restrict__ s, int64_t lds,
+                                                          uint8_t* __restrict__ qt, int64_t ldqt,
+                                                          float* __restrict__ st, int64_t ldst,
+                                                          int64_t tiles, int64_t ktiles) {
+  __shared__ __align__(16) uint8_t tile[2][128 * 128];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // copy plan (as in requant_kernel): copy j of wave w moves rows
+  // 32 j + 8 w .. + 7, lane l fills LDS chunk l % 8 of its row with global
+  // chunk (l % 8) ^ swizzle(row)
+  const int crow = 8 * wave + (lane >> 3);
+  const uint32_t ldq32 = static_cast<uint32_t>(ldq);
+  uint32_t voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 32 * j + crow;
+    voff[j] = static_cast<uint32_t>(r) * ldq32 + static_cast<uint32_t>((lane & 7) ^ (2 * ((r >> 4) & 3))) * 16u;
+  }
+  const uint32_t lds_tile = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&tile[0][0]));
+  auto issue = [&](int64_t t, int buf) {
+    const int64_t nb = t / ktiles, kb = t - nb * ktiles;
+    const i32x4 rs = make_rsrc(q + nb * 128 * ldq + kb * 128, 128u * ldq32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      copy16_to_lds(rs, voff[j], 0u, lds_tile + buf * 16384 + (4 * j + wave) * 1024);
+  };
+
+  const int tg = tid & 7;   // rows 16 tg .. 16 tg + 15 of the block
+  const int cg = tid >> 3;  // dword cg of every row: columns 4 cg .. 4 cg + 3
+  const int dw = cg ^ (8 * (tg & 3));
+
+  int64_t t = blockIdx.x;
+  if (t < tiles) issue(t, 0);
+  for (int it = 0; t < tiles; ++it) {
+    const int buf = it & 1;
+    const int64_t tn = t + gridDim.x;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // tile t landed (and earlier stores are done)
+    block_barrier();                            // every wave is done with the other buffer
+    if (tn < tiles) issue(tn, buf ^ 1);
+
+    const int64_t nb = t / ktiles, kb = t - nb * ktiles;
+    const uint8_t* tb = &tile[buf][0];
+    uint32_t out[4][4];  // out[c][i]: bytes of rows 16 tg + 4 i .. + 3 in column 4 cg + c
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t w[4], tr[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = *reinterpret_cast<const uint32_t*>(tb + (16 * tg + 4 * i + k) * 128 + dw * 4);
+      transpose4x4(w, tr);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) out[c][i] = tr[c];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint8_t* dst = qt + (kb * 128 + 4 * cg + c) * ldqt + nb * 128 + 16 * tg;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(out[c][0], out[c][1], out[c][2], out[c][3]);
+    }
+    if (tid == 0) st[kb * ldst + nb] = s[nb * lds + kb];
+    t = tn;
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
 }  // namespace
 
 hipError_t launch_requant_T_128x1(bool src_bf16, const void* in, const float* s_in, int64_t T,
@@ -162,6 +256,18 @@ hipError_t launch_requant_T_128x1(bool src_bf16, const void* in, const float* s_
   else
     hipLaunchKernelGGL(requant_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, src,
                        s_in, T, ld_in, lds_in, q_out, ld_out, s_out, lds_out, tiles, CB);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_w_128x128(const uint8_t* q, int64_t N, int64_t K, int64_t ldq,
+                                      const float* s, int64_t lds, uint8_t* qt, int64_t ldqt,
+                                      float* st, int64_t ldst, hipStream_t stream) {
+  const int64_t ktiles = K / 128;
+  const int64_t tiles = (N / 128) * ktiles;
+  // four 32 KiB workgroups per compute unit of a 256-CU MI355X
+  const int64_t grid = tiles < 1024 ? tiles : 1024;
+  hipLaunchKernelGGL(transpose_w_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, q,
+                     ldq, s, lds, qt, ldqt, st, ldst, tiles, ktiles);
   return hipGetLastError();
 }
 

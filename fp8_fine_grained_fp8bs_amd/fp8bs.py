@@ -32,7 +32,8 @@ SRC_FP8_1x128 = 0
 SRC_BF16 = 1
 
 ENTRY_POINTS = ("fp8bs_quant_act_1x128", "fp8bs_quant_w_128x128", "fp8bs_requant_T_128x1",
-                "fp8bs_gemm", "fp8bs_grouped_gemm", "fp8bs_status_string", "fp8bs_version")
+                "fp8bs_transpose_w_128x128", "fp8bs_gemm", "fp8bs_grouped_gemm",
+                "fp8bs_status_string", "fp8bs_version")
 
 _lib = None
 
@@ -57,6 +58,7 @@ def load() -> ctypes.CDLL:
         "fp8bs_quant_act_1x128": [P, I64, I64, I64, P, I64, P, I64, P],
         "fp8bs_quant_w_128x128": [P, I64, I64, I64, P, I64, P, I64, P],
         "fp8bs_requant_T_128x1": [I, P, P, I64, I64, I64, I64, P, I64, P, I64, P],
+        "fp8bs_transpose_w_128x128": [P, I64, I64, I64, P, I64, P, I64, P, I64, P],
         "fp8bs_gemm": [P, P, I64, I64, P, P, I64, I64, I, P, I64, I, I64, I64, I64, P],
         "fp8bs_grouped_gemm": [P, P, I64, P, P, P, I32, I64, P, I, I64, I64, P],
     }
@@ -133,6 +135,14 @@ def fp8bs_requant_T_128x1(src, x, s_in, q_out, s_out, stream=None):
           _ptr(q_out), _ld(q_out), _ptr(s_out), _ld(s_out), _stream(stream))
 
 
+def fp8bs_transpose_w_128x128(q, s, qt, st, stream=None):
+    """Codes q [N][K] with 128x128 block scales s [N/128][K/128] -> their
+    transpose qt [K][N], st [K/128][N/128]."""
+    N, K = q.shape
+    _call("fp8bs_transpose_w_128x128", _ptr(q), N, K, _ld(q), _ptr(s), _ld(s), _ptr(qt), _ld(qt),
+          _ptr(st), _ld(st), _stream(stream))
+
+
 def fp8bs_gemm(a, sa, b, sb, bmode, d, dt, stream=None):
     """D [M][N] = A [M][K] * B [N][K]^T with block scales."""
     M, K = a.shape
@@ -181,6 +191,15 @@ def requant_T_128x1(x, s_in=None, stream=None):
     src = SRC_FP8_1x128 if s_in is not None else SRC_BF16
     fp8bs_requant_T_128x1(src, x, s_in, q, s, stream)
     return q, s
+
+
+def transpose_w_128x128(q, s, stream=None):
+    import torch
+    N, K = q.shape
+    qt = torch.empty((K, N), dtype=torch.uint8, device=q.device)
+    st = torch.empty((K // 128, N // 128), dtype=torch.float32, device=q.device)
+    fp8bs_transpose_w_128x128(q, s, qt, st, stream)
+    return qt, st
 
 
 def gemm(a, sa, b, sb, bmode=BSCALE_BLOCK_128x128, out_f32=False, stream=None):

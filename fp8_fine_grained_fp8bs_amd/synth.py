@@ -21,7 +21,9 @@ default; draws happen in the order written below):
                 remainder rounding to the total); A_up [T][7168] N(0,1),
                 W_up [E][4096][7168] N(0,0.01), A_down [T][2048] N(0,1),
                 W_down [E][7168][2048] N(0,0.01).  Default T=16384.
-* ``wgrad``     X [T][7168] and dY [T][2048] N(0, 0.01).  Default T=8192.
+* ``wgrad``     X [T][7168] and dY [T][2048] N(0, 0.01), then (only when
+                asked for) the layer weight W [2048][7168] N(0, 0.01) for the
+                input gradient dX = dY W.  Default T=8192.
 
 Sizes are parameters so tests can draw the same distributions at sizes the
 oracle finishes in seconds.
@@ -126,9 +128,13 @@ def moe(T=16384, E=8, K_up=7168, N_up=4096, K_down=2048, N_down=7168, seed=0,
     return out
 
 
-def wgrad(T=8192, C_in=7168, C_out=2048, seed=0):
-    """Backward weight-gradient inputs: X [T][C_in], dY [T][C_out]."""
+def wgrad(T=8192, C_in=7168, C_out=2048, seed=0, with_w=False):
+    """Backward inputs of one Linear layer: X [T][C_in], dY [T][C_out], and
+    (with_w) the layer's weight W [C_out][C_in] for the input gradient."""
     rng = np.random.default_rng(seed)
     x = _normal(rng, (T, C_in), 0.01)
     dy = _normal(rng, (T, C_out), 0.01)
-    return {"X": bf16_bits(x), "dY": bf16_bits(dy)}
+    out = {"X": bf16_bits(x), "dY": bf16_bits(dy)}
+    if with_w:
+        out["W"] = bf16_bits(_normal(rng, (C_out, C_in), 0.01))
+    return out

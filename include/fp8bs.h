@@ -115,6 +115,27 @@ fp8bs_status fp8bs_requant_T_128x1(fp8bs_requant_src src, const void *in, const 
                                    void *stream);
 
 /*
+ * Transpose of 128x128-block-quantized weights, for the backward pass for
+ * the input.  [p3] para 4: the backward pass is split into a part for the
+ * input and a part for the weights; [p1] para 3: weights are quantized in
+ * 128x128 blocks.  dX = dY W needs W as the B operand of fp8bs_gemm
+ * (K-contiguous), i.e. as W^T.  A block's max-abs does not depend on its
+ * orientation, so the quantized W^T is the transposed codes of W with the
+ * transposed scale grid (the same bits fp8bs_quant_w_128x128 gives for the
+ * bf16 W^T); nothing is re-quantized.
+ *   q   u8  [N][ldq]    codes of W            s   f32 [N/128][lds]    s[(n/128)*lds + k/128]
+ *   qt  u8  [K][ldqt]   qt[k*ldqt + n] = q[n*ldq + k]
+ *   st  f32 [K/128][ldst]  st[(k/128)*ldst + n/128] = s[(n/128)*lds + k/128]
+ * N >= 0 (0 is a no-op), K > 0; N % 128 == 0 and K % 128 == 0 (the
+ * transposed weight is the K-contiguous operand of a GEMM with K' = N),
+ * and a code row must span fewer than 2^25 bytes (ldq), else
+ * FP8BS_ERR_UNSUPPORTED_SHAPE.  q and qt must not overlap.
+ */
+fp8bs_status fp8bs_transpose_w_128x128(const uint8_t *q, int64_t N, int64_t K, int64_t ldq,
+                                       const float *s, int64_t lds, uint8_t *qt, int64_t ldqt,
+                                       float *st, int64_t ldst, void *stream);
+
+/*
  * Block-scaled FP8 GEMM, D = A * B^T, both operands K-contiguous.
  * [p1] para 2: per-group scales along K are multiplied in as part of
  * dequantization; [p1] para 3 and [p2] para 1: partial sums are promoted to

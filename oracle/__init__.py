@@ -9,8 +9,9 @@ The arithmetic lives in ``fp8bs_oracle.c`` (plain C, binary64 sums, binary32
 scales); this module only builds it, loads it with ctypes and marshals numpy
 arrays.  Each wrapper names the passage of the DeepSeek-V3 report excerpts
 (five web pages, cited as [p1] = xn--9g3bo1gtkw0l8ubf92bgle.kr post
-wr_id=32373, [p2] = why-be.why-be.co.kr post wr_id=73620, [p4] = bestpmk.kr
-post wr_id=299512, with a paragraph number) that it follows.
+wr_id=32373, [p2] = why-be.why-be.co.kr post wr_id=73620, [p3] =
+xn--9g3bo1gtkw0l8ubf92bgle.kr post wr_id=113503, [p4] = bestpmk.kr post
+wr_id=299512, with a paragraph number) that it follows.
 
 Parity status: every function below is pinned by ``tests/test_oracle_*.py``
 except :func:`gemm_unpromoted` (the limited-precision accumulation model,
@@ -213,6 +214,20 @@ def requant_T_128x1_bf16(x_bf16: np.ndarray):
     dummy = np.zeros(1, np.float32)
     _load().orc_requant_T_128x1(1, _p(x), _p(dummy), T, C, _p(qo), _p(so))
     return qo, so
+
+
+def transpose_w_128x128(q_in: np.ndarray, s_in: np.ndarray):
+    """Quantized W^T for the backward pass for the input ([p3] para 4 splits
+    the backward pass into the input and the weight parts; blocks of [p1]
+    para 3): q [N][K], s [N/128][K/128] -> (q^T [K][N], s^T [K/128][N/128]).
+    A 128x128 block's max-abs does not depend on its orientation, so these
+    are the codes and scales quant_w_128x128 gives for W^T (pinned in the
+    tests).  A pure data movement: no arithmetic."""
+    q = _u8(q_in)
+    s = _f32(s_in)
+    N, K = q.shape
+    assert N % 128 == 0 and K % 128 == 0 and s.shape == (N // 128, K // 128)
+    return np.ascontiguousarray(q.T), np.ascontiguousarray(s.T)
 
 
 def quant_per_tensor(x_bf16: np.ndarray):

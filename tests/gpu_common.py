@@ -110,3 +110,27 @@ def native_loaded():
     lib = fp8bs.load()
     assert lib.fp8bs_version() >= 100
     return lib
+
+
+def sample_idx(M, N, n=3000, seed=0):
+    rng = np.random.default_rng(seed)
+    mi = np.concatenate([rng.integers(0, M, n), [0, M - 1, 0, M - 1], np.full(64, M // 2)])
+    ni = np.concatenate([rng.integers(0, N, n), [0, 0, N - 1, N - 1], np.arange(64) * (N // 64)])
+    return mi, ni
+
+
+def sampled_check(name, qa, sa, qb, sb, d32_dev, d16_dev=None, bmode=oracle.BSCALE_BLOCK):
+    """FP32 result on sampled entries vs the oracle; the BF16 result (if
+    given) on every entry vs the rounded FP32 result."""
+    M, N = qa.shape[0], qb.shape[0]
+    mi, ni = sample_idx(M, N)
+    ref = oracle.gemm_entries(qa, sa, qb, sb, mi, ni, bmode)
+    mag = gemm_mag(qa, sa, qb, sb, bmode, mi, ni)
+    d32 = host(d32_dev)
+    fro, worst = check_f32_gemm(name, d32[mi, ni], ref, mag)
+    msg = f"{name}: sampled f32 rel-fro {fro:.2e} max-err/sum|ab| {worst:.2e}"
+    if d16_dev is not None:
+        d16 = host(d16_dev)
+        check_bf16_is_rounded_f32(name, d16, d32)
+        msg += f"; bf16 == RNE(f32) on all {d16.size}; sampled flips vs rounded oracle {bf16_flips(d16[mi, ni], ref)}"
+    announce(msg)

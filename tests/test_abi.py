@@ -46,6 +46,10 @@ def requant(src=0, x=A, s_in=A, T=256, C=128, ld_in=128, lds_in=1, q=A, ld_out=2
     return fp8bs.load().fp8bs_requant_T_128x1(src, x, s_in, T, C, ld_in, lds_in, q, ld_out, s_out, lds_out, NULL)
 
 
+def transpose_w(q=A, N=256, K=384, ldq=384, s=A, lds=3, qt=A, ldqt=256, st=A, ldst=2):
+    return fp8bs.load().fp8bs_transpose_w_128x128(q, N, K, ldq, s, lds, qt, ldqt, st, ldst, NULL)
+
+
 def gemm(a=A, sa=A, lda=256, ldsa=2, b=A, sb=A, ldb=256, ldsb=2, bmode=0, d=A, ldd=64, dt=0,
          M=8, N=64, K=256):
     return fp8bs.load().fp8bs_gemm(a, sa, lda, ldsa, b, sb, ldb, ldsb, bmode, d, ldd, dt, M, N, K, NULL)
@@ -86,6 +90,23 @@ def grouped(a=A, sa=A, ldsa=2, b=A, sb=A, off=A, E=2, M=10, d=A, dt=0, N=128, K=
     (lambda: requant(ld_out=264), fp8bs.ERR_MISALIGNED),
     (lambda: requant(ld_in=1 << 25), fp8bs.ERR_UNSUPPORTED_SHAPE),
     (lambda: requant(T=0), fp8bs.OK),
+    (lambda: transpose_w(N=-128), fp8bs.ERR_INVALID_ARG),
+    (lambda: transpose_w(K=0), fp8bs.ERR_INVALID_ARG),
+    (lambda: transpose_w(N=200, ldqt=208), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: transpose_w(K=320, ldq=320), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: transpose_w(q=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: transpose_w(s=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: transpose_w(qt=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: transpose_w(st=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: transpose_w(ldq=256), fp8bs.ERR_INVALID_ARG),
+    (lambda: transpose_w(lds=2), fp8bs.ERR_INVALID_ARG),
+    (lambda: transpose_w(ldqt=128), fp8bs.ERR_INVALID_ARG),
+    (lambda: transpose_w(ldst=1), fp8bs.ERR_INVALID_ARG),
+    (lambda: transpose_w(q=A + 8), fp8bs.ERR_MISALIGNED),
+    (lambda: transpose_w(ldqt=264), fp8bs.ERR_MISALIGNED),
+    (lambda: transpose_w(st=A + 1), fp8bs.ERR_MISALIGNED),
+    (lambda: transpose_w(ldq=1 << 25), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: transpose_w(N=0), fp8bs.OK),
     (lambda: gemm(bmode=2), fp8bs.ERR_INVALID_ARG),
     (lambda: gemm(dt=9), fp8bs.ERR_INVALID_ARG),
     (lambda: gemm(K=192, lda=256, ldb=256), fp8bs.ERR_UNSUPPORTED_SHAPE),
@@ -120,6 +141,7 @@ def test_valid_call_without_gpu_reports_no_device():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert quant_act() == fp8bs.ERR_NO_DEVICE
+    assert transpose_w() == fp8bs.ERR_NO_DEVICE
     assert gemm() == fp8bs.ERR_NO_DEVICE
 
 

@@ -7,7 +7,8 @@ import torch
 import oracle
 from fp8_fine_grained_fp8bs_amd import fp8bs, synth
 from tests.gpu_common import (announce, bf16_flips, check_bf16_is_rounded_f32, check_f32_gemm,
-                              dev, f32_dev, gemm_mag, host, native_loaded, u8_dev)
+                              dev, f32_dev, gemm_mag, host, native_loaded, sampled_check,
+                              u8_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,30 +42,6 @@ def _full_check(name, qa, sa, qb, sb, bmode=oracle.BSCALE_BLOCK, pads=(0, 0, 0, 
     check_bf16_is_rounded_f32(name + " bf16", d16, d32)
     flips = bf16_flips(d16, ref)
     announce(f"{name}: f32 rel-fro {fro:.2e} max-err/sum|ab| {worst:.2e}; bf16 flips vs rounded oracle {flips}/{ref.size}")
-
-
-def _sample_idx(M, N, n=3000, seed=0):
-    rng = np.random.default_rng(seed)
-    mi = np.concatenate([rng.integers(0, M, n), [0, M - 1, 0, M - 1], np.full(64, M // 2)])
-    ni = np.concatenate([rng.integers(0, N, n), [0, 0, N - 1, N - 1], np.arange(64) * (N // 64)])
-    return mi, ni
-
-
-def _sampled_check(name, qa, sa, qb, sb, d32_dev, d16_dev=None, bmode=oracle.BSCALE_BLOCK):
-    """FP32 result on sampled entries vs the oracle; the BF16 result (if
-    given) on every entry vs the rounded FP32 result."""
-    M, N = qa.shape[0], qb.shape[0]
-    mi, ni = _sample_idx(M, N)
-    ref = oracle.gemm_entries(qa, sa, qb, sb, mi, ni, bmode)
-    mag = gemm_mag(qa, sa, qb, sb, bmode, mi, ni)
-    d32 = host(d32_dev)
-    fro, worst = check_f32_gemm(name, d32[mi, ni], ref, mag)
-    msg = f"{name}: sampled f32 rel-fro {fro:.2e} max-err/sum|ab| {worst:.2e}"
-    if d16_dev is not None:
-        d16 = host(d16_dev)
-        check_bf16_is_rounded_f32(name, d16, d32)
-        msg += f"; bf16 == RNE(f32) on all {d16.size}; sampled flips vs rounded oracle {bf16_flips(d16[mi, ni], ref)}"
-    announce(msg)
 
 
 def test_gemm_tiny_full():
@@ -146,7 +123,7 @@ def test_gemm_mlp_up_full_size_sampled():
     sad, sbd = f32_dev(sa), f32_dev(sb)
     out = fp8bs.gemm(a, sad, b, sbd)
     out32 = fp8bs.gemm(a, sad, b, sbd, out_f32=True)
-    _sampled_check("mlp_up", qa, sa, qb, sb, out32, out)
+    sampled_check("mlp_up", qa, sa, qb, sb, out32, out)
     assert torch.isfinite(out32).all()
 
 
@@ -160,7 +137,7 @@ def test_gemm_wgrad_row_mode_full_size_sampled():
     qa, sa = oracle.requant_T_128x1_fp8(q1, s1)          # [7168][8192]
     qb, sb = oracle.requant_T_128x1_bf16(d["dY"])        # [2048][8192]
     out = fp8bs.gemm(u8_dev(qa), f32_dev(sa), u8_dev(qb), f32_dev(sb), fp8bs.BSCALE_ROW_1x128, out_f32=True)
-    _sampled_check("wgrad", qa, sa, qb, sb, out, None, bmode=oracle.BSCALE_ROW)
+    sampled_check("wgrad", qa, sa, qb, sb, out, None, bmode=oracle.BSCALE_ROW)
 
 
 def _grouped_dev(qa, sa, qb, sb, off, out_f32):
@@ -218,6 +195,41 @@ def test_grouped_moe_full_size_sampled(which):
     check_bf16_is_rounded_f32(f"grouped {which} bf16", d16, d32)
     announce(f"grouped {which}: sampled f32 rel-fro {fro:.2e} max-err/sum|ab| {worst:.2e}; "
              f"bf16 flips vs rounded oracle {bf16_flips(d16[mi, ni], ref)}")
+
+
+def test_gemm_bf16_output_rounding_crafted_values():
+    """The BF16 epilogue rounds every FP32 result once to nearest-even.  With
+    a[m] = 1.0 at k = 0 (zero elsewhere), b[n] = 1.0 at k = 0 and sb = 1, the
+    FP32 result of row m is exactly sa[m], so chosen scales put chosen FP32
+    values through the epilogue: random bit patterns, bf16 ties with even
+    and odd last bits, values next to ties, FP32 subnormals, and the top of
+    the range (rounding up to infinity)."""
+    native_loaded()
+    rng = np.random.default_rng(21)
+    rand = rng.integers(0, 0x7F800000, 40000, dtype=np.uint32) | (rng.integers(0, 2, 40000, dtype=np.uint32) << 31)
+    hi = rng.integers(0x0001, 0x7F7F, 6000, dtype=np.uint32) << 16
+    crafted = np.concatenate([
+        hi | 0x8000, hi | 0x7FFF, hi | 0x8001, hi | 0x0001, hi | 0xFFFF,         # ties and neighbours
+        rng.integers(1, 0x00800000, 4000, dtype=np.uint32),                      # FP32 subnormals
+        np.array([0x7F7FFFFF, 0x7F7F8000, 0x7F7F7FFF, 0x7F7EFFFF, 0x00000001, 0x00008000,
+                  0x00018000, 0x007FFFFF, 0x00800000, 0x3F808000, 0x3F818000], np.uint32)])
+    crafted = crafted | (rng.integers(0, 2, crafted.size, dtype=np.uint32) << 31)
+    pats = np.concatenate([rand, crafted])
+    pats = pats[pats != 0x80000000]           # -0 becomes +0 when added to the zero accumulator
+    sa_vals = pats.view(np.float32)
+    M, N, K = sa_vals.size, 48, 128
+    qa = np.zeros((M, K), np.uint8); qa[:, 0] = 0x38
+    qb = np.zeros((N, K), np.uint8); qb[:, 0] = 0x38
+    sa = sa_vals.reshape(M, 1).copy()
+    sb = np.ones((1, 1), np.float32)
+    announce(f"bf16 epilogue rounding on {M} crafted FP32 values")
+    d32 = _gemm_dev(qa, sa, qb, sb, oracle.BSCALE_BLOCK, True)
+    assert np.array_equal(d32.view(np.uint32), np.repeat(pats.reshape(M, 1), N, 1)), "FP32 path is not exact"
+    d16 = _gemm_dev(qa, sa, qb, sb, oracle.BSCALE_BLOCK, False)
+    ref = oracle.round_to_bf16(sa_vals.astype(np.float64))
+    bad = np.flatnonzero(d16[:, 0] != ref)
+    assert bad.size == 0, f"{bad.size} wrong roundings, first {pats[bad[0]]:#010x} -> {d16[bad[0], 0]:#06x}, want {ref[bad[0]]:#06x}"
+    assert (d16 == d16[:, :1]).all()
 
 
 def test_gemm_deterministic():

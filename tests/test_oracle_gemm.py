@@ -77,6 +77,27 @@ def test_gemm_integer_codes_equal_int_matmul():
     assert np.array_equal(d, (ia.astype(np.int64) @ ib.T.astype(np.int64)).astype(np.float64))
 
 
+def test_input_gradient_through_transposed_weight_equals_int_matmul():
+    """dX = dY W with dY [T][C_out] and W [C_out][C_in]: the GEMM takes the
+    transposed quantized weight as its B operand.  Integer codes with unit
+    scales make the exact product an int64 matmul, so a wrongly oriented
+    operand or scale grid fails."""
+    rng = np.random.default_rng(6)
+    T, C_out, C_in = 16, 256, 384
+    idy = rng.integers(-16, 17, (T, C_out)); iw = rng.integers(-16, 17, (C_out, C_in))
+    import torch
+    enc = lambda v: torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    qdy, qw = enc(idy), enc(iw)
+    sdy = np.ones((T, C_out // 128), np.float32)
+    sw = (2.0 ** rng.integers(-3, 4, (C_out // 128, C_in // 128))).astype(np.float32)
+    qwt, swt = oracle.transpose_w_128x128(qw, sw)
+    d = oracle.gemm(qdy, sdy, qwt, swt)
+    # exact: sum over C_out of dy * w * scale of w's block
+    scale = np.repeat(np.repeat(sw, 128, 0), 128, 1).astype(np.float64)      # [C_out][C_in]
+    ref = idy.astype(np.float64) @ (iw * scale)
+    assert np.array_equal(d, ref)
+
+
 def test_gemm_scale_linearity_and_block_vs_row():
     q = synth.tiny(M=40, N=200, K=384)
     qa, sa = oracle.quant_act_1x128(q["A"])

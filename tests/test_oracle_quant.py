@@ -157,6 +157,24 @@ def test_quant_w_transpose_invariance():
     assert np.array_equal(st, s.T)
 
 
+def test_transpose_w_equals_quantization_of_transposed_weight():
+    """The quantized W^T of the input-gradient pass is the quantization of
+    the bf16 W^T: transposing the codes and the scale grid must give the
+    same bits as quantizing W^T block by block."""
+    w = synth.wgrad(T=256, C_in=384, C_out=256, with_w=True)["W"]       # [256][384]
+    rng = np.random.default_rng(11)
+    w = w.copy()
+    w[rng.random(w.shape) < 0.01] ^= 0x0100       # perturb exponents: varied block max-abs
+    q, s = oracle.quant_w_128x128(w)
+    qt, st = oracle.transpose_w_128x128(q, s)
+    q2, s2 = oracle.quant_w_128x128(np.ascontiguousarray(w.T))
+    assert qt.shape == (384, 256) and st.shape == (3, 2)
+    assert np.array_equal(qt, q2) and np.array_equal(st.view(np.uint32), s2.view(np.uint32))
+    # and it is an involution
+    q3, s3 = oracle.transpose_w_128x128(qt, st)
+    assert np.array_equal(q3, q) and np.array_equal(s3, s)
+
+
 def test_requant_fp8_composition_bruteforce():
     """requant_T(q, s1) equals the exact 128-token quantization of the FP32
     dequantized values fl32(dec(q) * s1), transposed; ragged T."""
