@@ -12,8 +12,10 @@ included).  Each kernel is also timed with HIP events on the stream it runs
 on; the GEMM is the dominant kernel and its roofline fraction is reported
 against the MI355X dense FP8 peak.
 
-The other hot-path rows (backward 1x128 -> 128x1 re-quantization, the
-weight-gradient GEMM with row scales, and the grouped MoE GEMMs with their
+The other hot-path rows (the up-projection GEMM with its output quantized
+for the next layer, fused and unfused; backward 1x128 -> 128x1
+re-quantization, the weight-gradient GEMM with row scales, the weight
+transpose and input-gradient GEMM; the grouped MoE GEMMs with their
 quantization) are timed the same way after the step and reported under
 "rows"; they are not part of ``value``.
 
@@ -145,6 +147,46 @@ def cpu_baseline(x_u16, w_u16, M, N, K):
                        f"({t_qw:.2f} s), GEMM of {g_rows}/{M} rows x {N} x {K} ({t_g:.2f} s); "
                        f"extrapolated to the full step = {est:.1f} s"),
             "seconds_measured": t_qa + t_qw + t_g}
+
+
+def time_fused(dev, qx, sx, qw, sw, Y, reps=20, warm=3):
+    """The up-projection GEMM with its output quantized for the next layer:
+    fused into the epilogue, and unfused (BF16 GEMM, then quant_act of Y)."""
+    import torch
+    from fp8_fine_grained_fp8bs_amd import fp8bs
+    M, K = qx.shape
+    N = qw.shape[0]
+    qy = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    sy = torch.empty((M, N // 128), dtype=torch.float32, device=dev)
+    kt = KernelTimer()
+    log("rows: fused output quantization")
+
+    def fused():
+        kt.run("fused", lambda: fp8bs.fp8bs_gemm_quant_1x128(qx, sx, qw, sw, fp8bs.BSCALE_BLOCK_128x128, qy, sy))
+
+    def unfused():
+        kt.run("u_gemm", lambda: fp8bs.fp8bs_gemm(qx, sx, qw, sw, fp8bs.BSCALE_BLOCK_128x128, Y, fp8bs.OUT_BF16))
+        kt.run("u_quant", lambda: fp8bs.fp8bs_quant_act_1x128(Y, qy, sy))
+
+    for fn in (fused, unfused):
+        for _ in range(warm):
+            fn()
+    kt.reset()
+    for _ in range(reps):
+        fused()
+        unfused()
+    torch.cuda.synchronize()
+    fl = 2.0 * M * N * K
+    ms_f = kt.mean_ms("fused")
+    ms_u = kt.mean_ms("u_gemm") + kt.mean_ms("u_quant")
+    return {
+        "gemm_quant_1x128": {"shape": f"M{M} N{N} K{K}, E4M3 out + 1x128 scales", "us": ms_f * 1e3,
+                             "TFLOP/s": fl / ms_f / 1e9, "frac_fp8_peak": fl / ms_f / 1e9 / FP8_PEAK_TFLOPS},
+        "gemm_bf16_then_quant_act": {"shape": f"M{M} N{N} K{K}, BF16 out, then quant_act of [{M}][{N}]",
+                                     "us": ms_u * 1e3, "TFLOP/s": fl / ms_u / 1e9,
+                                     "frac_fp8_peak": fl / ms_u / 1e9 / FP8_PEAK_TFLOPS,
+                                     "quant_act_us": kt.mean_ms("u_quant") * 1e3},
+    }
 
 
 def time_rows(dev, reps=20, warm=3):
@@ -330,7 +372,9 @@ def main():
         "kernels": kernels,
     }
     if args.rows == "all":
-        result["rows"] = time_rows(dev)
+        rows = time_fused(dev, qx, sx, qw, sw, Y)
+        rows.update(time_rows(dev))
+        result["rows"] = rows
     if args.cpu_baseline == "on":
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(d["X"], d["W"], M, N, K)

@@ -179,8 +179,33 @@ fp8bs_status fp8bs_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t 
     return FP8BS_ERR_UNSUPPORTED_SHAPE;
   FP8BS_TRY(check_device());
   return launched(fp8bs::launch_gemm(a, sa, lda, ldsa, b, sb, ldb, ldsb,
-                                     bmode == FP8BS_BSCALE_ROW_1x128, d, ldd, dt == FP8BS_OUT_F32,
-                                     M, N, K, static_cast<hipStream_t>(stream)));
+                                     bmode == FP8BS_BSCALE_ROW_1x128, d, ldd, nullptr, 0,
+                                     dt == FP8BS_OUT_F32 ? 1 : 0, M, N, K,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+fp8bs_status fp8bs_gemm_quant_1x128(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa,
+                                    const uint8_t* b, const float* sb, int64_t ldb, int64_t ldsb,
+                                    fp8bs_bscale bmode, uint8_t* q, int64_t ldq, float* s,
+                                    int64_t lds, int64_t M, int64_t N, int64_t K, void* stream) {
+  if (bmode != FP8BS_BSCALE_BLOCK_128x128 && bmode != FP8BS_BSCALE_ROW_1x128)
+    return FP8BS_ERR_INVALID_ARG;
+  if (M < 0 || N < 0 || K <= 0) return FP8BS_ERR_INVALID_ARG;
+  if (K % 128 != 0 || N % 128 != 0) return FP8BS_ERR_UNSUPPORTED_SHAPE;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  FP8BS_TRY(check_matrix(a, K, lda, 1));
+  FP8BS_TRY(check_matrix(b, K, ldb, 1));
+  FP8BS_TRY(check_scales(sa, K / 128, ldsa));
+  FP8BS_TRY(check_scales(sb, K / 128, ldsb));
+  FP8BS_TRY(check_matrix(q, N, ldq, 1));
+  FP8BS_TRY(check_scales(s, N / 128, lds));
+  if (lda >= kMaxCodeStride || ldb >= kMaxCodeStride || ldsa >= kMaxScaleStride ||
+      ldsb >= kMaxScaleStride)
+    return FP8BS_ERR_UNSUPPORTED_SHAPE;
+  FP8BS_TRY(check_device());
+  return launched(fp8bs::launch_gemm(a, sa, lda, ldsa, b, sb, ldb, ldsb,
+                                     bmode == FP8BS_BSCALE_ROW_1x128, q, ldq, s, lds, 2, M, N, K,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 fp8bs_status fp8bs_grouped_gemm(const uint8_t* a, const float* sa, int64_t ldsa,

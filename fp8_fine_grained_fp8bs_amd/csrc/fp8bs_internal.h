@@ -25,8 +25,8 @@ hipError_t launch_transpose_w_128x128(const uint8_t* q, int64_t N, int64_t K, in
 
 hipError_t launch_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa,
                        const uint8_t* b, const float* sb, int64_t ldb, int64_t ldsb,
-                       bool bscale_row, void* d, int64_t ldd, bool out_f32,
-                       int64_t M, int64_t N, int64_t K, hipStream_t st);
+                       bool bscale_row, void* d, int64_t ldd, float* s_out, int64_t lds_out,
+                       int out, int64_t M, int64_t N, int64_t K, hipStream_t st);
 
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, int64_t ldsa,
                                const uint8_t* b, const float* sb, const int32_t* offsets,

@@ -118,9 +118,10 @@ struct GemmArgs {
   const float* sa;
   const uint8_t* b;
   const float* sb;
-  void* d;
+  void* d;                 // output (E4M3 codes when the output is quantized)
+  float* s_out;            // 1x128 scales of a quantized output
   const int32_t* offsets;  // grouped only
-  int64_t lda, ldsa, ldb, ldsb, ldd;
+  int64_t lda, ldsa, ldb, ldsb, ldd, lds_out;
   int64_t M, N, K;
   int32_t E;               // grouped only
   int32_t tiles_m;         // (upper bound of) M tiles
@@ -377,8 +378,14 @@ __device__ __forceinline__ void compute_lds(v4f (&acc)[C::MB][C::NB], const uint
   __builtin_amdgcn_s_setprio(0);
 }
 
-template <class C, bool OUT_F32, bool BROW, bool GROUPED>
+// Output forms of the epilogue.
+constexpr int kOutBf16 = 0;  // BF16, nearest-even
+constexpr int kOutF32 = 1;   // FP32
+constexpr int kOutFp8 = 2;   // E4M3 codes + one FP32 scale per 1x128 tile along N
+
+template <class C, int OUT, bool BROW, bool GROUPED>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
+  constexpr bool OUT_F32 = OUT == kOutF32;
   constexpr int BM = C::BM, BN = C::BN;
   static_assert(C::lds_bytes(BROW) <= 160 * 1024, "LDS budget");
   __shared__ __align__(16) uint8_t lds[C::lds_bytes(BROW)];
@@ -655,7 +662,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     //      pass), so that every global store writes 16 contiguous bytes per
     //      lane and a wave writes whole output rows.  Lane (fr, kc) holds
     //      columns 4 kc .. 4 kc + 3 of row fr of each 16x16 block.
-    constexpr int OB = OUT_F32 ? 4 : 2;           // output bytes per element
+    constexpr int OB = OUT == kOutBf16 ? 2 : 4;   // staged bytes per element
     constexpr int ROWB = BN * OB + 16;            // padded LDS row
     constexpr int CPR = BN * OB / 16;             // 16-byte chunks per tile row
     constexpr int PR0 = C::STAGE / ROWB;          // rows that fit one stage
@@ -681,7 +688,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
             const int c = wn * (C::NB * 16) + j * 16 + 4 * kc;
             const v4f vv = acc[i][j];
             uint8_t* dst = ob + r * ROWB + c * OB;
-            if (OUT_F32) {
+            if (OUT != kOutBf16) {
               *reinterpret_cast<float4*>(dst) = make_float4(vv[0], vv[1], vv[2], vv[3]);
             } else {
               *reinterpret_cast<uint2*>(dst) =
@@ -692,19 +699,51 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
       }
       __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);  // this wave's LDS writes are done
       block_barrier();
-#pragma unroll 4
-      for (int ch = tid; ch < PR * CPR; ch += C::NT) {
-        const int r = ch / CPR, cc = ch % CPR;
-        const int64_t m = cm0 + pass * PR + r;
-        const int c0 = cc * (16 / OB);
-        if (m >= cm_end || c0 >= cols) continue;
-        const uint4 vv = *reinterpret_cast<const uint4*>(ob + r * ROWB + cc * 16);
-        uint8_t* dst = dbase + m * ldd_b + (cn0 + c0) * OB;
-        if (c0 + 16 / OB <= cols) {
-          *reinterpret_cast<uint4*>(dst) = vv;
-        } else {
-          const uint8_t* src = reinterpret_cast<const uint8_t*>(&vv);
-          for (int e = 0; e < (cols - c0) * OB; ++e) dst[e] = src[e];
+      if (OUT == kOutFp8) {
+        // quantize the staged FP32 rows as 1x128 tiles along N: one 16-lane
+        // DPP row per tile, 8 values per lane, every lane active for the
+        // row max-abs; tiles past M or N are computed and not stored
+        constexpr int GPR = BN / 128;                // tiles per tile row
+        constexpr int UNITS = PR * GPR;
+        static_assert(UNITS % (C::NT / 16) == 0, "quantized output passes");
+        const int sub = lane & 15;
+        uint8_t* const qbase = static_cast<uint8_t*>(p.d);
+#pragma unroll
+        for (int u0 = 0; u0 < UNITS; u0 += C::NT / 16) {
+          const int u = u0 + (tid >> 4);
+          const int r = u / GPR, gc = u % GPR;
+          const float* src = reinterpret_cast<const float*>(ob + r * ROWB + (gc * 128 + sub * 8) * 4);
+          const float4 x0 = *reinterpret_cast<const float4*>(src);
+          const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+          const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          float am = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(v[e]));
+          am = row16_max(am);
+          const TileScale ts = make_tile_scale(am);
+          const uint2 cw = make_uint2(encode4(v, ts), encode4(v + 4, ts));
+          const int64_t m = cm0 + pass * PR + r;
+          const int c0 = gc * 128;
+          if (m < cm_end && c0 < cols) {
+            *reinterpret_cast<uint2*>(qbase + m * p.ldd + cn0 + c0 + sub * 8) = cw;
+            if (sub == 0) p.s_out[m * p.lds_out + (cn0 + c0) / 128] = ts.s;
+          }
+        }
+      } else {
+  #pragma unroll 4
+        for (int ch = tid; ch < PR * CPR; ch += C::NT) {
+          const int r = ch / CPR, cc = ch % CPR;
+          const int64_t m = cm0 + pass * PR + r;
+          const int c0 = cc * (16 / OB);
+          if (m >= cm_end || c0 >= cols) continue;
+          const uint4 vv = *reinterpret_cast<const uint4*>(ob + r * ROWB + cc * 16);
+          uint8_t* dst = dbase + m * ldd_b + (cn0 + c0) * OB;
+          if (c0 + 16 / OB <= cols) {
+            *reinterpret_cast<uint4*>(dst) = vv;
+          } else {
+            const uint8_t* src = reinterpret_cast<const uint8_t*>(&vv);
+            for (int e = 0; e < (cols - c0) * OB; ++e) dst[e] = src[e];
+          }
         }
       }
     }
@@ -713,7 +752,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
 }
 
 template <class C, bool BROW, bool GROUPED>
-hipError_t dispatch(GemmArgs args, int64_t tiles_m_extra, bool out_f32, hipStream_t st) {
+hipError_t dispatch(GemmArgs args, int64_t tiles_m_extra, int out, hipStream_t st) {
   const int64_t tm = (args.M + C::BM - 1) / C::BM + tiles_m_extra, tn = (args.N + C::BN - 1) / C::BN;
   if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
   args.tiles_m = static_cast<int32_t>(tm);
@@ -722,8 +761,12 @@ hipError_t dispatch(GemmArgs args, int64_t tiles_m_extra, bool out_f32, hipStrea
   // multiple of the XCD count), each walking tiles gridDim.x apart
   const int64_t vt = tm * tn;
   const dim3 grid(static_cast<unsigned>(vt < 256 ? vt : 256)), block(C::NT);
-  if (out_f32) hipLaunchKernelGGL((gemm_kernel<C, true, BROW, GROUPED>), grid, block, 0, st, args);
-  else hipLaunchKernelGGL((gemm_kernel<C, false, BROW, GROUPED>), grid, block, 0, st, args);
+  if (out == kOutF32) hipLaunchKernelGGL((gemm_kernel<C, kOutF32, BROW, GROUPED>), grid, block, 0, st, args);
+  else if (out == kOutFp8) {
+    if constexpr (GROUPED) return hipErrorInvalidValue;  // not offered for the grouped form
+    else hipLaunchKernelGGL((gemm_kernel<C, kOutFp8, BROW, GROUPED>), grid, block, 0, st, args);
+  }
+  else hipLaunchKernelGGL((gemm_kernel<C, kOutBf16, BROW, GROUPED>), grid, block, 0, st, args);
   return hipGetLastError();
 }
 
@@ -731,14 +774,15 @@ hipError_t dispatch(GemmArgs args, int64_t tiles_m_extra, bool out_f32, hipStrea
 
 hipError_t launch_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa,
                        const uint8_t* b, const float* sb, int64_t ldb, int64_t ldsb,
-                       bool bscale_row, void* d, int64_t ldd, bool out_f32,
-                       int64_t M, int64_t N, int64_t K, hipStream_t st) {
+                       bool bscale_row, void* d, int64_t ldd, float* s_out, int64_t lds_out,
+                       int out, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   GemmArgs args{};
   args.a = a; args.sa = sa; args.b = b; args.sb = sb; args.d = d; args.offsets = nullptr;
+  args.s_out = s_out; args.lds_out = lds_out;
   args.lda = lda; args.ldsa = ldsa; args.ldb = ldb; args.ldsb = ldsb; args.ldd = ldd;
   args.M = M; args.N = N; args.K = K; args.E = 0;
-  if (bscale_row) return dispatch<RowCfg, true, false>(args, 0, out_f32, st);
-  return dispatch<MainCfg, false, false>(args, 0, out_f32, st);
+  if (bscale_row) return dispatch<RowCfg, true, false>(args, 0, out, st);
+  return dispatch<MainCfg, false, false>(args, 0, out, st);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, int64_t ldsa,
@@ -751,7 +795,7 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, int64_t ldsa,
   args.M = M_total; args.N = N; args.K = K; args.E = E;
   // upper bound of the per-expert M-tile count: each expert adds at most one
   // partial tile
-  return dispatch<MainCfg, false, true>(args, E, out_f32, st);
+  return dispatch<MainCfg, false, true>(args, E, out_f32 ? kOutF32 : kOutBf16, st);
 }
 
 }  // namespace fp8bs

@@ -32,7 +32,8 @@ SRC_FP8_1x128 = 0
 SRC_BF16 = 1
 
 ENTRY_POINTS = ("fp8bs_quant_act_1x128", "fp8bs_quant_w_128x128", "fp8bs_requant_T_128x1",
-                "fp8bs_transpose_w_128x128", "fp8bs_gemm", "fp8bs_grouped_gemm",
+                "fp8bs_transpose_w_128x128", "fp8bs_gemm", "fp8bs_gemm_quant_1x128",
+                "fp8bs_grouped_gemm",
                 "fp8bs_status_string", "fp8bs_version")
 
 _lib = None
@@ -60,6 +61,7 @@ def load() -> ctypes.CDLL:
         "fp8bs_requant_T_128x1": [I, P, P, I64, I64, I64, I64, P, I64, P, I64, P],
         "fp8bs_transpose_w_128x128": [P, I64, I64, I64, P, I64, P, I64, P, I64, P],
         "fp8bs_gemm": [P, P, I64, I64, P, P, I64, I64, I, P, I64, I, I64, I64, I64, P],
+        "fp8bs_gemm_quant_1x128": [P, P, I64, I64, P, P, I64, I64, I, P, I64, P, I64, I64, I64, I64, P],
         "fp8bs_grouped_gemm": [P, P, I64, P, P, P, I32, I64, P, I, I64, I64, P],
     }
     for name, args in sigs.items():
@@ -151,6 +153,15 @@ def fp8bs_gemm(a, sa, b, sb, bmode, d, dt, stream=None):
           int(bmode), _ptr(d), _ld(d), int(dt), M, N, K, _stream(stream))
 
 
+def fp8bs_gemm_quant_1x128(a, sa, b, sb, bmode, q, s, stream=None):
+    """D = A [M][K] * B [N][K]^T, quantized in 1x128 tiles along N:
+    q u8 [M][N], s f32 [M][N/128]."""
+    M, K = a.shape
+    N = b.shape[0]
+    _call("fp8bs_gemm_quant_1x128", _ptr(a), _ptr(sa), _ld(a), _ld(sa), _ptr(b), _ptr(sb), _ld(b),
+          _ld(sb), int(bmode), _ptr(q), _ld(q), _ptr(s), _ld(s), M, N, K, _stream(stream))
+
+
 def fp8bs_grouped_gemm(a, sa, b, sb, offsets, d, dt, stream=None):
     """Per-expert D rows = A rows * B[e]^T; offsets int32 [E+1] on the device."""
     M_total, K = a.shape
@@ -208,6 +219,15 @@ def gemm(a, sa, b, sb, bmode=BSCALE_BLOCK_128x128, out_f32=False, stream=None):
     d = torch.empty((M, N), dtype=torch.float32 if out_f32 else torch.bfloat16, device=a.device)
     fp8bs_gemm(a, sa, b, sb, bmode, d, OUT_F32 if out_f32 else OUT_BF16, stream)
     return d
+
+
+def gemm_quant_1x128(a, sa, b, sb, bmode=BSCALE_BLOCK_128x128, stream=None):
+    import torch
+    M, N = a.shape[0], b.shape[0]
+    q = torch.empty((M, N), dtype=torch.uint8, device=a.device)
+    s = torch.empty((M, N // 128), dtype=torch.float32, device=a.device)
+    fp8bs_gemm_quant_1x128(a, sa, b, sb, bmode, q, s, stream)
+    return q, s
 
 
 def grouped_gemm(a, sa, b, sb, offsets, out_f32=False, stream=None):

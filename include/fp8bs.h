@@ -157,6 +157,28 @@ fp8bs_status fp8bs_gemm(const uint8_t *a, const float *sa, int64_t lda, int64_t 
                         int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
+ * Block-scaled FP8 GEMM whose result leaves already quantized for the next
+ * layer: the quantization of the output activations is fused into the
+ * GEMM's epilogue, so the output crosses HBM once, as E4M3 codes, instead
+ * of being written in BF16 and read back by fp8bs_quant_act_1x128 ([p2]
+ * para 1 describes that round trip as the cost of separate quantization).
+ * D is computed as by fp8bs_gemm (FP32 per-group promotion); each 1x128
+ * tile of D along N (row m, columns 128j .. 128j+127) is then quantized
+ * from its FP32 values as fp8bs_quant_act_1x128 quantizes a tile:
+ * s = fl32(amax / 448), q = nearest-even E4M3 of d / s, saturated.
+ *   a, sa, b, sb, bmode   as for fp8bs_gemm
+ *   q  u8  [M][ldq]       E4M3 codes of D
+ *   s  f32 [M][lds]       s[m*lds + n/128]
+ * M >= 0, N >= 0 (either 0 is a no-op), K > 0; K % 128 == 0 and
+ * N % 128 == 0, else FP8BS_ERR_UNSUPPORTED_SHAPE (also for the stride
+ * limits of fp8bs_gemm).
+ */
+fp8bs_status fp8bs_gemm_quant_1x128(const uint8_t *a, const float *sa, int64_t lda, int64_t ldsa,
+                                    const uint8_t *b, const float *sb, int64_t ldb, int64_t ldsb,
+                                    fp8bs_bscale bmode, uint8_t *q, int64_t ldq, float *s,
+                                    int64_t lds, int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
  * Grouped block-scaled GEMM for the experts one GPU holds, with ragged
  * token counts (the per-expert FP8 GEMMs of the MoE layers; [p2] para 2).
  * Rows offsets[e] .. offsets[e+1]-1 of A are multiplied by expert e:

@@ -258,6 +258,17 @@ def gemm(a, sa, b, sb, bmode: int = BSCALE_BLOCK) -> np.ndarray:
     return d
 
 
+def gemm_quant_1x128(a, sa, b, sb, bmode: int = BSCALE_BLOCK):
+    """The GEMM with the next layer's activation quantization fused into its
+    output ([p2] para 1: quantizing separately costs a BF16 write and read
+    back): D = A * B^T rounded once to FP32, then 1x128 tiles along N
+    quantized as quant_act_1x128 does ([p1] para 3).  Returns (codes [M][N],
+    scales [M][N/128])."""
+    d = gemm(a, sa, b, sb, bmode)
+    assert d.shape[1] % 128 == 0
+    return quant_act_1x128_f32(d.astype(np.float32))
+
+
 def gemm_entries(a, sa, b, sb, mi, ni, bmode: int = BSCALE_BLOCK) -> np.ndarray:
     a = _u8(a); b = _u8(b); sa = _f32(sa); sb = _f32(sb)
     mi = np.ascontiguousarray(mi, dtype=np.int64)

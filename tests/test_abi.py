@@ -55,6 +55,12 @@ def gemm(a=A, sa=A, lda=256, ldsa=2, b=A, sb=A, ldb=256, ldsb=2, bmode=0, d=A, l
     return fp8bs.load().fp8bs_gemm(a, sa, lda, ldsa, b, sb, ldb, ldsb, bmode, d, ldd, dt, M, N, K, NULL)
 
 
+def gemm_quant(a=A, sa=A, lda=256, ldsa=2, b=A, sb=A, ldb=256, ldsb=2, bmode=0, q=A, ldq=128, s=A,
+               lds=1, M=8, N=128, K=256):
+    return fp8bs.load().fp8bs_gemm_quant_1x128(a, sa, lda, ldsa, b, sb, ldb, ldsb, bmode, q, ldq, s, lds,
+                                               M, N, K, NULL)
+
+
 def grouped(a=A, sa=A, ldsa=2, b=A, sb=A, off=A, E=2, M=10, d=A, dt=0, N=128, K=256):
     return fp8bs.load().fp8bs_grouped_gemm(a, sa, ldsa, b, sb, off, E, M, d, dt, N, K, NULL)
 
@@ -121,6 +127,20 @@ def grouped(a=A, sa=A, ldsa=2, b=A, sb=A, off=A, E=2, M=10, d=A, dt=0, N=128, K=
     (lambda: gemm(ldsb=1 << 22), fp8bs.ERR_UNSUPPORTED_SHAPE),
     (lambda: gemm(M=0), fp8bs.OK),
     (lambda: gemm(N=0), fp8bs.OK),
+    (lambda: gemm_quant(bmode=3), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm_quant(N=192, ldq=192, lds=2), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: gemm_quant(K=200, lda=256, ldb=256), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: gemm_quant(M=-2), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm_quant(q=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm_quant(s=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm_quant(ldq=64), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm_quant(lds=0), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm_quant(q=A + 8), fp8bs.ERR_MISALIGNED),
+    (lambda: gemm_quant(ldq=136), fp8bs.ERR_MISALIGNED),
+    (lambda: gemm_quant(s=A + 2), fp8bs.ERR_MISALIGNED),
+    (lambda: gemm_quant(lda=1 << 24), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: gemm_quant(M=0), fp8bs.OK),
+    (lambda: gemm_quant(N=0), fp8bs.OK),
     (lambda: grouped(E=0), fp8bs.ERR_INVALID_ARG),
     (lambda: grouped(off=NULL), fp8bs.ERR_INVALID_ARG),
     (lambda: grouped(off=A + 2), fp8bs.ERR_MISALIGNED),
@@ -142,6 +162,7 @@ def test_valid_call_without_gpu_reports_no_device():
         pytest.skip("a GPU is present")
     assert quant_act() == fp8bs.ERR_NO_DEVICE
     assert transpose_w() == fp8bs.ERR_NO_DEVICE
+    assert gemm_quant() == fp8bs.ERR_NO_DEVICE
     assert gemm() == fp8bs.ERR_NO_DEVICE
 
 
