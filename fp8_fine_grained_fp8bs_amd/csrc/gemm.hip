@@ -22,11 +22,10 @@
 //   product inside each 8-product chunk, so promoting once per group is what
 //   bounds the error, as on the hardware the report describes.)
 // * The MFMA "A" operand is the B tile and its "B" operand the A tile, so
-//   each lane ends up holding 4 consecutive output columns of one row:
-//   8-byte (BF16) or 16-byte (FP32) stores in the epilogue, and one A-scale
-//   per lane per 16-row block.
+//   each lane ends up holding 4 consecutive output columns of one row and
+//   needs one A-scale per 16-row block.
 // * Workgroup tile 128 (M) x 256 (N), 512 threads = 2 x 4 waves of 64 x 64
-//   (other shapes selectable with FP8BS_GEMM_CFG).
+//   (row-mode B scales: 128 x 128, 2 x 4 waves of 64 x 32).
 //   The A tile (16 KiB) and B tile (32 KiB) of a K group are copied
 //   global -> LDS by the load unit itself (buffer_load_dwordx4 ... lds: no
 //   staging registers, no LDS write instructions), into three LDS stages:
@@ -47,7 +46,9 @@
 //   in that XCD's L2.
 // * Workgroups are persistent (one per compute unit): after a tile's last
 //   K group the first K groups of the workgroup's next tile are copied while
-//   the finished tile goes out through LDS with 16-byte stores.
+//   the finished tile goes out through LDS with 16-byte stores, as BF16,
+//   FP32, or E4M3 codes with one scale per 1x128 tile along N (the next
+//   layer's activation quantization fused into the epilogue).
 #include <hip/hip_runtime.h>
 
 #include "fp8bs_device.h"
@@ -64,14 +65,12 @@ constexpr int NUM_XCD = 8;
 constexpr int SBLK = 4;        // K groups per scale block
 constexpr int NSLOT = 3;       // scale blocks resident in LDS
 
-// Workgroup tile BM x BN, WM x WN waves of (BM/WM) x (BN/WN).
-// NSTAGE = 3: fragments of the next K group are read from LDS while the
-// current one is multiplied (two fragment register sets); NSTAGE = 2: each
-// group's fragments are read at the start of its own step (one set, for
-// wave tiles too large to double-buffer).
-template <int BM_, int BN_, int WM_, int WN_, int NSTAGE_ = 3>
+// Workgroup tile BM x BN, WM x WN waves of (BM/WM) x (BN/WN), three LDS
+// stages: the fragments of the next K group are read from LDS while the
+// current one is multiplied (two fragment register sets).
+template <int BM_, int BN_, int WM_, int WN_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NSTAGE = NSTAGE_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NSTAGE = 3;
   static constexpr int NW = WM * WN;              // waves
   static constexpr int NT = 64 * NW;              // threads
   static constexpr int MB = BM / WM / 16;         // 16-row blocks per wave
@@ -96,20 +95,7 @@ struct Cfg {
   static_assert(BM % 64 == 0 && BN % 64 == 0, "scale copies move 16-row units, SBLK per lane row");
 };
 
-#ifndef FP8BS_GEMM_CFG
-#define FP8BS_GEMM_CFG 2
-#endif
-#if FP8BS_GEMM_CFG == 0
-using MainCfg = Cfg<256, 128, 4, 2>;
-#elif FP8BS_GEMM_CFG == 1
-using MainCfg = Cfg<128, 128, 2, 2>;
-#elif FP8BS_GEMM_CFG == 2
 using MainCfg = Cfg<128, 256, 2, 4>;
-#elif FP8BS_GEMM_CFG == 3
-using MainCfg = Cfg<256, 256, 2, 4, 2>;
-#else
-using MainCfg = Cfg<256, 128, 2, 2, 3>;
-#endif
 // Row-scale mode holds 16 more scales per fragment set: narrower wave tiles.
 using RowCfg = Cfg<128, 128, 2, 4>;
 
@@ -215,29 +201,6 @@ __device__ __forceinline__ void load_frag(Frag<C>& f, const uint8_t* stage, cons
   }
 }
 
-// One K group from registers: MB x NB MFMAs and their promotions per wave.
-template <class C, bool BROW>
-__device__ __forceinline__ void compute(v4f (&acc)[C::MB][C::NB], const Frag<C>& f) {
-  // Keep the matrix core fed: raise this wave's issue priority for the MFMA
-  // block and let the scheduler interleave the other work with the MFMAs.
-  __builtin_amdgcn_s_setprio(1);
-  __builtin_amdgcn_iglp_opt(0);
-#pragma unroll
-  for (int i = 0; i < C::MB; ++i) {
-    const float sc = f.sam[i] * f.sbv;
-#pragma unroll
-    for (int j = 0; j < C::NB; ++j) {
-      const v4f part = mfma_16x16x128_fp8(f.fb[j], f.fa[i]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float s = BROW ? f.sam[i] * f.sbn[j][q] : sc;
-        acc[i][j][q] = __builtin_fmaf(part[q], s, acc[i][j][q]);
-      }
-    }
-  }
-  __builtin_amdgcn_s_setprio(0);
-}
-
 // Software-pipelined K group for the three-stage path.  The MFMAs of the
 // current group are issued one per step; each step also promotes the
 // partial of the MFMA issued LAG steps earlier, issues one read of the next
@@ -320,60 +283,6 @@ __device__ __forceinline__ void pipelined_group(v4f (&acc)[C::MB][C::NB], const 
       for (int k = (s - 1) * COPIES / (S - 1); k < s * COPIES / (S - 1); ++k) issue_part(k);
     }
     __builtin_amdgcn_sched_barrier(0);
-  }
-  __builtin_amdgcn_s_setprio(0);
-}
-
-// One K group straight from an LDS stage (two-stage pipeline): the B-tile
-// fragments are read once, the A-tile fragments block by block with the
-// next block's read issued before the current block's MFMAs.
-template <class C, bool BROW>
-__device__ __forceinline__ void compute_lds(v4f (&acc)[C::MB][C::NB], const uint8_t* stage,
-                                            const float* slot, int gq, int wm, int wn, int lane) {
-  const uint8_t* la = stage;
-  const uint8_t* lb = stage + C::A_BYTES;
-  const float* lsb = slot + C::SA_BYTES / 4;
-  const int fr = lane & 15;
-  const int kc = lane >> 4;
-  v8i fb[C::NB];
-#pragma unroll
-  for (int j = 0; j < C::NB; ++j) {
-    const int r = (wn * C::NB + j) * 16 + fr;
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(lb + swz(r, kc));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(lb + swz(r, kc + 4));
-    fb[j] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-  }
-  float sbn[C::NB][4];
-  float sbv = 0.0f;
-  if (BROW) {
-#pragma unroll
-    for (int j = 0; j < C::NB; ++j) {
-      const float4 v = *reinterpret_cast<const float4*>(lsb + ((wn * C::NB + j) * SBLK + gq) * 16 + 4 * kc);
-      sbn[j][0] = v.x; sbn[j][1] = v.y; sbn[j][2] = v.z; sbn[j][3] = v.w;
-    }
-  } else {
-    sbv = lsb[gq * 16 + (wn * C::NB * 16) / 128];
-  }
-  __builtin_amdgcn_s_setprio(1);
-  __builtin_amdgcn_iglp_opt(0);
-#pragma unroll
-  for (int i = 0; i < C::MB; ++i) {
-    const int rb = wm * C::MB + i;
-    const int r = rb * 16 + fr;
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(la + swz(r, kc));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(la + swz(r, kc + 4));
-    const v8i fa = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    const float sam = slot[(rb * SBLK + gq) * 16 + fr];
-    const float sc = sam * sbv;
-#pragma unroll
-    for (int j = 0; j < C::NB; ++j) {
-      const v4f part = mfma_16x16x128_fp8(fb[j], fa);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float s = BROW ? sam * sbn[j][q] : sc;
-        acc[i][j][q] = __builtin_fmaf(part[q], s, acc[i][j][q]);
-      }
-    }
   }
   __builtin_amdgcn_s_setprio(0);
 }
