@@ -120,6 +120,17 @@ fp8bs_status fp8bs_quant_w_128x128(const void* w, int64_t N, int64_t K, int64_t 
                                                 s, lds, static_cast<hipStream_t>(stream)));
 }
 
+fp8bs_status fp8bs_quant_per_tensor(const void* x, int64_t n, uint8_t* q, float* s, void* stream) {
+  if (n < 0) return FP8BS_ERR_INVALID_ARG;
+  if (n % 128 != 0) return FP8BS_ERR_UNSUPPORTED_SHAPE;
+  if (n == 0) return FP8BS_OK;
+  if (x == nullptr || q == nullptr || s == nullptr) return FP8BS_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return FP8BS_ERR_MISALIGNED;
+  FP8BS_TRY(check_device());
+  return launched(fp8bs::launch_quant_per_tensor(static_cast<const uint16_t*>(x), n, q, s,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 fp8bs_status fp8bs_requant_T_128x1(fp8bs_requant_src src, const void* in, const float* s_in,
                                    int64_t T, int64_t C, int64_t ld_in, int64_t lds_in,
                                    uint8_t* q_out, int64_t ld_out, float* s_out, int64_t lds_out,

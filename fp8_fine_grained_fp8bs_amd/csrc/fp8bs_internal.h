@@ -14,6 +14,9 @@ hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, int64
                                   uint8_t* q, int64_t ldq, float* s, int64_t lds,
                                   hipStream_t st);
 
+hipError_t launch_quant_per_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* s,
+                                   hipStream_t st);
+
 hipError_t launch_requant_T_128x1(bool src_bf16, const void* in, const float* s_in,
                                   int64_t T, int64_t C, int64_t ld_in, int64_t lds_in,
                                   uint8_t* q_out, int64_t ld_out, float* s_out,

@@ -202,7 +202,66 @@ __global__ __launch_bounds__(256) void quant_w_kernel(const uint16_t* __restrict
   }
 }
 
+// ---------------------------------------------------------------------
+// Per-tensor scaling, the practice [p3] para 4 describes (the tensor's
+// max-abs mapped to the FP8 maximum) and [p1] para 4 contrasts with the
+// fine-grained tiles; kept as the comparison path of the accuracy study.
+// Three passes over a contiguous bf16 tensor whose length is a multiple of
+// 128: the max-abs (one atomic max per wave on the bit pattern, which
+// orders like the magnitude for non-negative values), the codes, and the
+// scale.  The scale word holds the max-abs bits between the passes.
+// ---------------------------------------------------------------------
+__global__ void per_tensor_init_kernel(uint32_t* __restrict__ s_bits) { *s_bits = 0u; }
+
+__global__ __launch_bounds__(256) void per_tensor_amax_kernel(const uint16_t* __restrict__ x,
+                                                              int64_t chunks,
+                                                              uint32_t* __restrict__ s_bits) {
+  uint32_t m = 0;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; c < chunks;
+       c += static_cast<int64_t>(gridDim.x) * 256) {
+    const uint4 v = load16_nt(x + c * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = max(m, max(w[k] & 0x7fffu, (w[k] >> 16) & 0x7fffu));
+  }
+  const float am = wave_max(__uint_as_float(m << 16));
+  if ((threadIdx.x & 63) == 0) atomicMax(s_bits, __float_as_uint(am));
+}
+
+__global__ __launch_bounds__(256) void per_tensor_quant_kernel(const uint16_t* __restrict__ x,
+                                                               int64_t chunks,
+                                                               const uint32_t* __restrict__ s_bits,
+                                                               uint8_t* __restrict__ q) {
+  const TileScale t = make_tile_scale(__uint_as_float(*s_bits));
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; c < chunks;
+       c += static_cast<int64_t>(gridDim.x) * 256) {
+    const uint4 v = load16_nt(x + c * 8);
+    const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                        bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    *reinterpret_cast<uint2*>(q + c * 8) = make_uint2(encode4(f, t), encode4(f + 4, t));
+  }
+}
+
+__global__ void per_tensor_finish_kernel(uint32_t* __restrict__ s_bits) {
+  *reinterpret_cast<float*>(s_bits) = make_tile_scale(__uint_as_float(*s_bits)).s;
+}
+
 }  // namespace
+
+hipError_t launch_quant_per_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* s,
+                                   hipStream_t st) {
+  const int64_t chunks = n / 8;
+  int64_t blocks = (chunks + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  uint32_t* sb = reinterpret_cast<uint32_t*>(s);
+  hipLaunchKernelGGL(per_tensor_init_kernel, dim3(1), dim3(1), 0, st, sb);
+  hipLaunchKernelGGL(per_tensor_amax_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, x,
+                     chunks, sb);
+  hipLaunchKernelGGL(per_tensor_quant_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                     x, chunks, sb, q);
+  hipLaunchKernelGGL(per_tensor_finish_kernel, dim3(1), dim3(1), 0, st, sb);
+  return hipGetLastError();
+}
 
 // Persistent form: 2 tile-quads per work item, 32 waves per compute unit
 // of a 256-CU MI355X.

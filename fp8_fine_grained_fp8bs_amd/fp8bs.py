@@ -31,7 +31,8 @@ BSCALE_ROW_1x128 = 1
 SRC_FP8_1x128 = 0
 SRC_BF16 = 1
 
-ENTRY_POINTS = ("fp8bs_quant_act_1x128", "fp8bs_quant_w_128x128", "fp8bs_requant_T_128x1",
+ENTRY_POINTS = ("fp8bs_quant_act_1x128", "fp8bs_quant_w_128x128", "fp8bs_quant_per_tensor",
+                "fp8bs_requant_T_128x1",
                 "fp8bs_transpose_w_128x128", "fp8bs_gemm", "fp8bs_gemm_quant_1x128",
                 "fp8bs_grouped_gemm",
                 "fp8bs_status_string", "fp8bs_version")
@@ -58,6 +59,7 @@ def load() -> ctypes.CDLL:
     sigs = {
         "fp8bs_quant_act_1x128": [P, I64, I64, I64, P, I64, P, I64, P],
         "fp8bs_quant_w_128x128": [P, I64, I64, I64, P, I64, P, I64, P],
+        "fp8bs_quant_per_tensor": [P, I64, P, P, P],
         "fp8bs_requant_T_128x1": [I, P, P, I64, I64, I64, I64, P, I64, P, I64, P],
         "fp8bs_transpose_w_128x128": [P, I64, I64, I64, P, I64, P, I64, P, I64, P],
         "fp8bs_gemm": [P, P, I64, I64, P, P, I64, I64, I, P, I64, I, I64, I64, I64, P],
@@ -128,6 +130,12 @@ def fp8bs_quant_w_128x128(w, q, s, stream=None):
           _stream(stream))
 
 
+def fp8bs_quant_per_tensor(x, q, s, stream=None):
+    """x bf16 (contiguous, n % 128 == 0) -> q u8 (same shape), s f32 [1]."""
+    assert x.is_contiguous() and q.is_contiguous()
+    _call("fp8bs_quant_per_tensor", _ptr(x), x.numel(), _ptr(q), _ptr(s), _stream(stream))
+
+
 def fp8bs_requant_T_128x1(src, x, s_in, q_out, s_out, stream=None):
     """x [T][C] (codes with s_in [T][C/128], or bf16) -> q_out [C][T],
     s_out [C][ceil(T/128)]."""
@@ -189,6 +197,14 @@ def quant_w_128x128(w, stream=None):
     q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
     s = torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32, device=w.device)
     fp8bs_quant_w_128x128(w, q, s, stream)
+    return q, s
+
+
+def quant_per_tensor(x, stream=None):
+    import torch
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    s = torch.empty((1,), dtype=torch.float32, device=x.device)
+    fp8bs_quant_per_tensor(x, q, s, stream)
     return q, s
 
 

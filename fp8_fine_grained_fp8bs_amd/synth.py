@@ -11,7 +11,8 @@ default; draws happen in the order written below):
 * float32 draws are rounded to bf16 by round-to-nearest-even on the bit
   pattern (``bf16_bits``); wider draws are first rounded to float32.
 * ``tiny``      A [M][K] N(0,1) with an iid 1 % mask of entries multiplied by
-                50 (outliers); W [N][K] N(0, 0.02).  Default 128x512, 256x512.
+                50 (outliers; the factor is a parameter for the accuracy
+                study); W [N][K] N(0, 0.02).  Default 128x512, 256x512.
 * ``probe``     A, W [R][K] U(-1,1), each row multiplied by 10^u, u ~ U(-2,2).
                 Default M=N=1024, K=4096.
 * ``mlp_up``    X [T][K] N(0,1) except a seeded 1 % of the K channels drawn
@@ -55,12 +56,12 @@ def _normal(rng, shape, std=1.0) -> np.ndarray:
     return x
 
 
-def tiny(M=128, N=256, K=512, seed=0):
-    """A with 1 % x50 outliers, W ~ N(0, 0.02)."""
+def tiny(M=128, N=256, K=512, seed=0, outlier=50.0):
+    """A with 1 % outliers (x50 by default), W ~ N(0, 0.02)."""
     rng = np.random.default_rng(seed)
     a = _normal(rng, (M, K))
     mask = rng.random((M, K)) < 0.01
-    a[mask] *= np.float32(50.0)
+    a[mask] *= np.float32(outlier)
     w = _normal(rng, (N, K), 0.02)
     return {"A": bf16_bits(a), "W": bf16_bits(w)}
 

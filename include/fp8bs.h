@@ -91,6 +91,20 @@ fp8bs_status fp8bs_quant_w_128x128(const void *w, int64_t N, int64_t K, int64_t 
                                    void *stream);
 
 /*
+ * Per-tensor scaling: one scale for a whole tensor, the common practice
+ * [p3] para 4 describes (the tensor's max-abs mapped to the FP8 maximum)
+ * and [p1] para 4 contrasts with the fine-grained tiles.  The comparison
+ * path of the accuracy study; its codes feed fp8bs_gemm with the scale
+ * broadcast into the scale arrays.
+ *   x  bf16 [n] (contiguous)     q  u8 [n]     s  f32 [1]
+ * s = fl32(amax / 448) over all n values, q[i] = nearest-even E4M3 of
+ * x[i] / s, saturated (as for a tile of fp8bs_quant_act_1x128).  s is also
+ * used as working memory during the call.  n >= 0 (0 is a no-op),
+ * n % 128 == 0, else FP8BS_ERR_UNSUPPORTED_SHAPE; x and q 16-byte aligned.
+ */
+fp8bs_status fp8bs_quant_per_tensor(const void *x, int64_t n, uint8_t *q, float *s, void *stream);
+
+/*
  * Backward re-quantization of 1x128 tiles into 128x1 tiles, transposed.
  * [p1] para 3: in the backward pass the activation tiles are converted
  * from 1x128 to 128x1; [p1] para 4: activations are cached in FP8 for the

@@ -42,6 +42,10 @@ def quant_w(w=A, N=4, K=256, ldw=256, q=A, ldq=256, s=A, lds=2):
     return fp8bs.load().fp8bs_quant_w_128x128(w, N, K, ldw, q, ldq, s, lds, NULL)
 
 
+def quant_pt(x=A, n=256, q=A, s=A):
+    return fp8bs.load().fp8bs_quant_per_tensor(x, n, q, s, NULL)
+
+
 def requant(src=0, x=A, s_in=A, T=256, C=128, ld_in=128, lds_in=1, q=A, ld_out=256, s_out=A, lds_out=2):
     return fp8bs.load().fp8bs_requant_T_128x1(src, x, s_in, T, C, ld_in, lds_in, q, ld_out, s_out, lds_out, NULL)
 
@@ -86,6 +90,15 @@ def grouped(a=A, sa=A, ldsa=2, b=A, sb=A, off=A, E=2, M=10, d=A, dt=0, N=128, K=
     (lambda: quant_w(ldq=100), fp8bs.ERR_INVALID_ARG),
     (lambda: quant_w(w=A + 2), fp8bs.ERR_MISALIGNED),
     (lambda: quant_w(N=0), fp8bs.OK),
+    (lambda: quant_pt(n=-128), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_pt(n=200), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: quant_pt(x=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_pt(q=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_pt(s=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_pt(x=A + 8), fp8bs.ERR_MISALIGNED),
+    (lambda: quant_pt(q=A + 4), fp8bs.ERR_MISALIGNED),
+    (lambda: quant_pt(s=A + 2), fp8bs.ERR_MISALIGNED),
+    (lambda: quant_pt(n=0, x=NULL, q=NULL, s=NULL), fp8bs.OK),
     (lambda: requant(src=7), fp8bs.ERR_INVALID_ARG),
     (lambda: requant(C=100, ld_in=128), fp8bs.ERR_UNSUPPORTED_SHAPE),
     (lambda: requant(T=-1), fp8bs.ERR_INVALID_ARG),
@@ -162,6 +175,7 @@ def test_valid_call_without_gpu_reports_no_device():
         pytest.skip("a GPU is present")
     assert quant_act() == fp8bs.ERR_NO_DEVICE
     assert transpose_w() == fp8bs.ERR_NO_DEVICE
+    assert quant_pt() == fp8bs.ERR_NO_DEVICE
     assert gemm_quant() == fp8bs.ERR_NO_DEVICE
     assert gemm() == fp8bs.ERR_NO_DEVICE
 

@@ -175,6 +175,20 @@ def test_transpose_w_equals_quantization_of_transposed_weight():
     assert np.array_equal(q3, q) and np.array_equal(s3, s)
 
 
+def test_quant_per_tensor_is_one_group_over_the_tensor():
+    """Per-tensor scaling is the tile quantization with the whole tensor as
+    one group: brute force over every value, and equal to quant_act_1x128
+    when the tensor is a single 1x128 row."""
+    x = synth.tiny(M=64, N=128, K=256)["A"]                  # with x50 outliers
+    q, s = oracle.quant_per_tensor(x)
+    cq, cs = quantize_group_exact(synth.bf16_to_f32(x).ravel())
+    assert s == cs and np.array_equal(q.ravel(), cq)
+    row = x[:1, :128]
+    q1, s1 = oracle.quant_per_tensor(np.ascontiguousarray(row))
+    qa, sa = oracle.quant_act_1x128(np.ascontiguousarray(row))
+    assert s1 == sa[0, 0] and np.array_equal(q1, qa)
+
+
 def test_requant_fp8_composition_bruteforce():
     """requant_T(q, s1) equals the exact 128-token quantization of the FP32
     dequantized values fl32(dec(q) * s1), transposed; ragged T."""
