@@ -229,6 +229,17 @@ def time_rows(dev, reps=20, warm=3):
     rows["requant_T_128x1_bf16"] = {"shape": f"[{T}][{C_out}] -> [{C_out}][{T}]", "us": ms * 1e3,
                                     "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / HBM_PEAK_GBS,
                                     "bytes": b}
+    # the activations cached in E5M6 instead: encode, then decode for the backward pass
+    ye = torch.empty((T, C_in // 2 * 3), dtype=torch.uint8, device=dev)
+    xe = torch.empty((T, C_in), dtype=torch.bfloat16, device=dev)
+    b = T * C_in * (2 + 1.5)
+    ms = timed("e5m6_enc", lambda: fp8bs.fp8bs_encode_e5m6(X, ye))
+    rows["encode_e5m6"] = {"shape": f"[{T}][{C_in}]", "us": ms * 1e3, "GB/s": b / ms / 1e6,
+                           "frac_hbm": b / ms / 1e6 / HBM_PEAK_GBS, "bytes": b}
+    ms = timed("e5m6_dec", lambda: fp8bs.fp8bs_decode_e5m6(ye, xe))
+    rows["decode_e5m6"] = {"shape": f"[{T}][{C_in}]", "us": ms * 1e3, "GB/s": b / ms / 1e6,
+                           "frac_hbm": b / ms / 1e6 / HBM_PEAK_GBS, "bytes": b}
+    del ye, xe
     ms = timed("wgrad", lambda: fp8bs.fp8bs_gemm(qxt, sxt, qdt, sdt, fp8bs.BSCALE_ROW_1x128, dW, fp8bs.OUT_F32))
     fl = 2.0 * C_in * C_out * T
     rows["gemm_wgrad_row_f32"] = {"shape": f"M{C_in} N{C_out} K{T}", "us": ms * 1e3,

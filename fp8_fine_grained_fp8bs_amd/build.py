@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8bs.so")
-SOURCES = ["api.hip", "quant.hip", "requant.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quant.hip", "requant.hip", "gemm.hip", "e5m6.hip"]
 ARCH = "gfx950"
 
 

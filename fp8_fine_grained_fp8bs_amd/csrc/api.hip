@@ -131,6 +131,30 @@ fp8bs_status fp8bs_quant_per_tensor(const void* x, int64_t n, uint8_t* q, float*
                                                  static_cast<hipStream_t>(stream)));
 }
 
+fp8bs_status fp8bs_encode_e5m6(const void* x, int64_t T, int64_t C, int64_t ldx, uint8_t* y,
+                               int64_t ldy, void* stream) {
+  if (T < 0 || C <= 0) return FP8BS_ERR_INVALID_ARG;
+  if (C % 128 != 0) return FP8BS_ERR_UNSUPPORTED_SHAPE;
+  if (T == 0) return FP8BS_OK;
+  FP8BS_TRY(check_matrix(x, C, ldx, 2));
+  FP8BS_TRY(check_matrix(y, C / 2 * 3, ldy, 1));
+  FP8BS_TRY(check_device());
+  return launched(fp8bs::launch_encode_e5m6(static_cast<const uint16_t*>(x), T, C, ldx, y, ldy,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+fp8bs_status fp8bs_decode_e5m6(const uint8_t* y, int64_t T, int64_t C, int64_t ldy, void* x,
+                               int64_t ldx, void* stream) {
+  if (T < 0 || C <= 0) return FP8BS_ERR_INVALID_ARG;
+  if (C % 128 != 0) return FP8BS_ERR_UNSUPPORTED_SHAPE;
+  if (T == 0) return FP8BS_OK;
+  FP8BS_TRY(check_matrix(y, C / 2 * 3, ldy, 1));
+  FP8BS_TRY(check_matrix(x, C, ldx, 2));
+  FP8BS_TRY(check_device());
+  return launched(fp8bs::launch_decode_e5m6(y, T, C, ldy, static_cast<uint16_t*>(x), ldx,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 fp8bs_status fp8bs_requant_T_128x1(fp8bs_requant_src src, const void* in, const float* s_in,
                                    int64_t T, int64_t C, int64_t ld_in, int64_t lds_in,
                                    uint8_t* q_out, int64_t ld_out, float* s_out, int64_t lds_out,

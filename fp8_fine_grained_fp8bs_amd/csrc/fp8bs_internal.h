@@ -17,6 +17,12 @@ hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, int64
 hipError_t launch_quant_per_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* s,
                                    hipStream_t st);
 
+hipError_t launch_encode_e5m6(const uint16_t* x, int64_t T, int64_t C, int64_t ldx, uint8_t* y,
+                              int64_t ldy, hipStream_t st);
+
+hipError_t launch_decode_e5m6(const uint8_t* y, int64_t T, int64_t C, int64_t ldy, uint16_t* x,
+                              int64_t ldx, hipStream_t st);
+
 hipError_t launch_requant_T_128x1(bool src_bf16, const void* in, const float* s_in,
                                   int64_t T, int64_t C, int64_t ld_in, int64_t lds_in,
                                   uint8_t* q_out, int64_t ld_out, float* s_out,

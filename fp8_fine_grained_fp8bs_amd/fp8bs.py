@@ -32,7 +32,7 @@ SRC_FP8_1x128 = 0
 SRC_BF16 = 1
 
 ENTRY_POINTS = ("fp8bs_quant_act_1x128", "fp8bs_quant_w_128x128", "fp8bs_quant_per_tensor",
-                "fp8bs_requant_T_128x1",
+                "fp8bs_encode_e5m6", "fp8bs_decode_e5m6", "fp8bs_requant_T_128x1",
                 "fp8bs_transpose_w_128x128", "fp8bs_gemm", "fp8bs_gemm_quant_1x128",
                 "fp8bs_grouped_gemm",
                 "fp8bs_status_string", "fp8bs_version")
@@ -60,6 +60,8 @@ def load() -> ctypes.CDLL:
         "fp8bs_quant_act_1x128": [P, I64, I64, I64, P, I64, P, I64, P],
         "fp8bs_quant_w_128x128": [P, I64, I64, I64, P, I64, P, I64, P],
         "fp8bs_quant_per_tensor": [P, I64, P, P, P],
+        "fp8bs_encode_e5m6": [P, I64, I64, I64, P, I64, P],
+        "fp8bs_decode_e5m6": [P, I64, I64, I64, P, I64, P],
         "fp8bs_requant_T_128x1": [I, P, P, I64, I64, I64, I64, P, I64, P, I64, P],
         "fp8bs_transpose_w_128x128": [P, I64, I64, I64, P, I64, P, I64, P, I64, P],
         "fp8bs_gemm": [P, P, I64, I64, P, P, I64, I64, I, P, I64, I, I64, I64, I64, P],
@@ -136,6 +138,18 @@ def fp8bs_quant_per_tensor(x, q, s, stream=None):
     _call("fp8bs_quant_per_tensor", _ptr(x), x.numel(), _ptr(q), _ptr(s), _stream(stream))
 
 
+def fp8bs_encode_e5m6(x, y, stream=None):
+    """bf16 x [T][C] -> packed E5M6 y u8 [T][>= 1.5 C]."""
+    T, C = x.shape
+    _call("fp8bs_encode_e5m6", _ptr(x), T, C, _ld(x), _ptr(y), _ld(y), _stream(stream))
+
+
+def fp8bs_decode_e5m6(y, x, stream=None):
+    """packed E5M6 y u8 [T][>= 1.5 C] -> bf16 x [T][C] (exact)."""
+    T, C = x.shape
+    _call("fp8bs_decode_e5m6", _ptr(y), T, C, _ld(y), _ptr(x), _ld(x), _stream(stream))
+
+
 def fp8bs_requant_T_128x1(src, x, s_in, q_out, s_out, stream=None):
     """x [T][C] (codes with s_in [T][C/128], or bf16) -> q_out [C][T],
     s_out [C][ceil(T/128)]."""
@@ -206,6 +220,21 @@ def quant_per_tensor(x, stream=None):
     s = torch.empty((1,), dtype=torch.float32, device=x.device)
     fp8bs_quant_per_tensor(x, q, s, stream)
     return q, s
+
+
+def encode_e5m6(x, stream=None):
+    import torch
+    T, C = x.shape
+    y = torch.empty((T, C // 2 * 3), dtype=torch.uint8, device=x.device)
+    fp8bs_encode_e5m6(x, y, stream)
+    return y
+
+
+def decode_e5m6(y, C, stream=None):
+    import torch
+    x = torch.empty((y.shape[0], C), dtype=torch.bfloat16, device=y.device)
+    fp8bs_decode_e5m6(y, x, stream)
+    return x
 
 
 def requant_T_128x1(x, s_in=None, stream=None):

@@ -105,6 +105,27 @@ fp8bs_status fp8bs_quant_w_128x128(const void *w, int64_t N, int64_t K, int64_t 
 fp8bs_status fp8bs_quant_per_tensor(const void *x, int64_t n, uint8_t *q, float *s, void *stream);
 
 /*
+ * The 12-bit E5M6 format for cached activations.  [p1] para 3: a custom
+ * E5M6 format is used for some activations cached for the backward pass.
+ * Layout (a reading; the pages give none): bit 11 sign, bits 10..6
+ * exponent with bias 15, bits 5..0 mantissa, IEEE conventions (exponent 0:
+ * subnormal mant * 2^-20; exponent 31: infinity or NaN); largest finite
+ * value 65024.  A row of C values is packed into 1.5 C bytes, value i in
+ * bits 12 i .. 12 i + 11, little-endian.
+ * Encoding rounds each bf16 value to the nearest E5M6 value, ties to the
+ * even mantissa, magnitudes from 65280 up to infinity (IEEE overflow).
+ * Every E5M6 value is a bf16 value, so decoding is exact; the decoded rows
+ * feed fp8bs_requant_T_128x1 with FP8BS_SRC_BF16 in the backward pass.
+ *   x  bf16 [T][ldx]     y  u8 [T][ldy]  (ldy in bytes, >= 1.5 C)
+ * T >= 0 (0 is a no-op), C > 0, C % 128 == 0, else
+ * FP8BS_ERR_UNSUPPORTED_SHAPE; 16-byte alignment as for every byte buffer.
+ */
+fp8bs_status fp8bs_encode_e5m6(const void *x, int64_t T, int64_t C, int64_t ldx, uint8_t *y,
+                               int64_t ldy, void *stream);
+fp8bs_status fp8bs_decode_e5m6(const uint8_t *y, int64_t T, int64_t C, int64_t ldy, void *x,
+                               int64_t ldx, void *stream);
+
+/*
  * Backward re-quantization of 1x128 tiles into 128x1 tiles, transposed.
  * [p1] para 3: in the backward pass the activation tiles are converted
  * from 1x128 to 128x1; [p1] para 4: activations are cached in FP8 for the

@@ -75,6 +75,10 @@ def _load():
         "orc_gemm_bf16_f32acc": (None, [P, P, I64, I64, I64, P]),
         "orc_gemm_unpromoted": (None, [P, F32, P, F32, I64, I64, I64, ctypes.c_int, ctypes.c_int, P]),
         "orc_quant_per_tensor": (None, [P, I64, P, P]),
+        "orc_e5m6_value": (ctypes.c_double, [ctypes.c_uint16]),
+        "orc_e5m6_encode": (ctypes.c_uint16, [ctypes.c_double]),
+        "orc_encode_e5m6": (None, [P, I64, I64, P]),
+        "orc_decode_e5m6": (None, [P, I64, I64, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -228,6 +232,39 @@ def transpose_w_128x128(q_in: np.ndarray, s_in: np.ndarray):
     N, K = q.shape
     assert N % 128 == 0 and K % 128 == 0 and s.shape == (N // 128, K // 128)
     return np.ascontiguousarray(q.T), np.ascontiguousarray(s.T)
+
+
+# --------------------------------------------------------------------------
+# E5M6 cached-activation format ([p1] para 3)
+# --------------------------------------------------------------------------
+
+def e5m6_value(code: int) -> float:
+    return float(_load().orc_e5m6_value(int(code)))
+
+
+def e5m6_encode(y: float) -> int:
+    return int(_load().orc_e5m6_encode(float(y)))
+
+
+def encode_e5m6(x_bf16: np.ndarray) -> np.ndarray:
+    """bf16 [T][C] -> packed E5M6 [T][1.5 C] bytes (value i of a row in bits
+    12 i .. 12 i + 11, little-endian); nearest-even, IEEE overflow."""
+    x = _u16(x_bf16)
+    T, C = x.shape
+    assert C % 2 == 0
+    y = np.empty((T, C // 2 * 3), np.uint8)
+    _load().orc_encode_e5m6(_p(x), T, C, _p(y))
+    return y
+
+
+def decode_e5m6(y_packed: np.ndarray, C: int) -> np.ndarray:
+    """packed E5M6 [T][1.5 C] -> bf16 [T][C] bit patterns (exact)."""
+    y = _u8(y_packed)
+    T = y.shape[0]
+    assert y.shape[1] == C // 2 * 3
+    x = np.empty((T, C), np.uint16)
+    _load().orc_decode_e5m6(_p(y), T, C, _p(x))
+    return x
 
 
 def quant_per_tensor(x_bf16: np.ndarray):

@@ -511,3 +511,100 @@ void orc_quant_per_tensor(const uint16_t *x, int64_t n, uint8_t *q, float *s)
     for (int64_t i = 0; i < n; ++i)
         q[i] = quantize_one((float)orc_bf16_value(x[i]), sc);
 }
+
+/* ------------------------------------------------------------------ */
+/* E5M6 cached-activation format ([p1] para 3 names a custom E5M6 format */
+/* for some cached activations; the layout below is the reading taken): */
+/* 12 bits, bit 11 sign, bits 10..6 exponent (bias 15), bits 5..0       */
+/* mantissa, IEEE conventions: exponent 0 subnormal (mant * 2^-20),      */
+/* exponent 31 infinity (mant 0) or NaN.                                 */
+/* ------------------------------------------------------------------ */
+
+double orc_e5m6_value(uint16_t code)
+{
+    int sign = (code >> 11) & 1;
+    int e = (code >> 6) & 31;
+    int m = code & 63;
+    double mag;
+    if (e == 31)
+        mag = m ? NAN : INFINITY;
+    else if (e == 0)
+        mag = ldexp((double)m, -20);
+    else
+        mag = ldexp((double)(64 + m), e - 21);
+    return sign ? -mag : mag;
+}
+
+/* Nearest E5M6 code of a binary64 value, ties to the even mantissa; values
+ * at or beyond the midpoint between the largest finite value and 2^16 round
+ * to infinity (IEEE round-to-nearest overflow).  Brute force over the
+ * ordered table of the 1984 non-negative finite magnitudes (codes 0..0x7BF
+ * are ordered by value). */
+static double g_m6[1984];
+static int g_m6_ready = 0;
+
+uint16_t orc_e5m6_encode(double y)
+{
+    if (!g_m6_ready) {
+        for (int c = 0; c < 1984; ++c)
+            g_m6[c] = orc_e5m6_value((uint16_t)c);
+        g_m6_ready = 1;
+    }
+    uint16_t sign = signbit(y) ? 0x800 : 0;
+    double a = fabs(y);
+    double top = g_m6[1983];
+    double over = top + 0.5 * (65536.0 - top); /* midpoint to 2^16 */
+    if (a >= over)
+        return sign | 0x7C0;                    /* infinity (ties go to even 2^16) */
+    if (a >= top)
+        return sign | 1983;
+    int lo = 0, hi = 1983;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (g_m6[mid] <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    if (g_m6[lo] == a)
+        return sign | (uint16_t)lo;
+    double midpoint = 0.5 * (g_m6[lo] + g_m6[hi]);
+    int pick;
+    if (a < midpoint)
+        pick = lo;
+    else if (a > midpoint)
+        pick = hi;
+    else
+        pick = (lo % 2 == 0) ? lo : hi;
+    return sign | (uint16_t)pick;
+}
+
+/* bf16 [T][C] -> packed E5M6 rows (value i of a row in bits 12 i .. 12 i + 11,
+ * little-endian), C even. */
+void orc_encode_e5m6(const uint16_t *x, int64_t T, int64_t C, uint8_t *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t i = 0; i < C; i += 2) {
+            uint16_t c0 = orc_e5m6_encode(orc_bf16_value(x[t * C + i]));
+            uint16_t c1 = orc_e5m6_encode(orc_bf16_value(x[t * C + i + 1]));
+            uint8_t *p = y + t * (C / 2 * 3) + i / 2 * 3;
+            p[0] = (uint8_t)(c0 & 0xFF);
+            p[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xF) << 4));
+            p[2] = (uint8_t)(c1 >> 4);
+        }
+}
+
+/* packed E5M6 rows -> bf16 (every E5M6 value is a bf16 value) */
+void orc_decode_e5m6(const uint8_t *y, int64_t T, int64_t C, uint16_t *x)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t i = 0; i < C; i += 2) {
+            const uint8_t *p = y + t * (C / 2 * 3) + i / 2 * 3;
+            uint16_t c0 = (uint16_t)(p[0] | ((p[1] & 0xF) << 8));
+            uint16_t c1 = (uint16_t)((p[1] >> 4) | (p[2] << 4));
+            x[t * C + i] = orc_bf16_round(orc_e5m6_value(c0));
+            x[t * C + i + 1] = orc_bf16_round(orc_e5m6_value(c1));
+        }
+}

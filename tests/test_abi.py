@@ -46,6 +46,14 @@ def quant_pt(x=A, n=256, q=A, s=A):
     return fp8bs.load().fp8bs_quant_per_tensor(x, n, q, s, NULL)
 
 
+def enc6(x=A, T=4, C=128, ldx=128, y=A, ldy=192):
+    return fp8bs.load().fp8bs_encode_e5m6(x, T, C, ldx, y, ldy, NULL)
+
+
+def dec6(y=A, T=4, C=128, ldy=192, x=A, ldx=128):
+    return fp8bs.load().fp8bs_decode_e5m6(y, T, C, ldy, x, ldx, NULL)
+
+
 def requant(src=0, x=A, s_in=A, T=256, C=128, ld_in=128, lds_in=1, q=A, ld_out=256, s_out=A, lds_out=2):
     return fp8bs.load().fp8bs_requant_T_128x1(src, x, s_in, T, C, ld_in, lds_in, q, ld_out, s_out, lds_out, NULL)
 
@@ -99,6 +107,19 @@ def grouped(a=A, sa=A, ldsa=2, b=A, sb=A, off=A, E=2, M=10, d=A, dt=0, N=128, K=
     (lambda: quant_pt(q=A + 4), fp8bs.ERR_MISALIGNED),
     (lambda: quant_pt(s=A + 2), fp8bs.ERR_MISALIGNED),
     (lambda: quant_pt(n=0, x=NULL, q=NULL, s=NULL), fp8bs.OK),
+    (lambda: enc6(T=-1), fp8bs.ERR_INVALID_ARG),
+    (lambda: enc6(C=0), fp8bs.ERR_INVALID_ARG),
+    (lambda: enc6(C=64, ldx=64, ldy=96), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: enc6(x=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: enc6(y=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: enc6(ldy=176), fp8bs.ERR_INVALID_ARG),
+    (lambda: enc6(ldy=200), fp8bs.ERR_MISALIGNED),
+    (lambda: enc6(x=A + 2), fp8bs.ERR_MISALIGNED),
+    (lambda: enc6(T=0, x=NULL, y=NULL), fp8bs.OK),
+    (lambda: dec6(ldx=64), fp8bs.ERR_INVALID_ARG),
+    (lambda: dec6(y=A + 4), fp8bs.ERR_MISALIGNED),
+    (lambda: dec6(C=200, ldx=208, ldy=304), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: dec6(T=0), fp8bs.OK),
     (lambda: requant(src=7), fp8bs.ERR_INVALID_ARG),
     (lambda: requant(C=100, ld_in=128), fp8bs.ERR_UNSUPPORTED_SHAPE),
     (lambda: requant(T=-1), fp8bs.ERR_INVALID_ARG),
@@ -176,6 +197,7 @@ def test_valid_call_without_gpu_reports_no_device():
     assert quant_act() == fp8bs.ERR_NO_DEVICE
     assert transpose_w() == fp8bs.ERR_NO_DEVICE
     assert quant_pt() == fp8bs.ERR_NO_DEVICE
+    assert enc6() == fp8bs.ERR_NO_DEVICE and dec6() == fp8bs.ERR_NO_DEVICE
     assert gemm_quant() == fp8bs.ERR_NO_DEVICE
     assert gemm() == fp8bs.ERR_NO_DEVICE
 

@@ -139,3 +139,74 @@ def test_bf16_round_against_exact_and_torch():
     ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     ours = oracle.round_to_bf16(f.astype(np.float64))
     assert np.array_equal(ours, ref)
+
+
+# ---------------------------------------------------------------------------
+# E5M6 (12-bit cached-activation format): codec pins
+# ---------------------------------------------------------------------------
+
+def _e5m6_table():
+    return np.array([oracle.e5m6_value(c) for c in range(4096)])
+
+
+def test_e5m6_code_space():
+    """Sign, 5-bit exponent (bias 15), 6-bit mantissa, IEEE conventions:
+    +-0, 2 x 63 subnormals, 2 x 1920 normals, 2 infinities, 2 x 63 NaNs;
+    the non-negative finite codes ordered by value; closed-form anchors."""
+    tab = _e5m6_table()
+    assert np.isnan(tab).sum() == 126
+    assert np.isinf(tab).sum() == 2 and tab[0x7C0] == np.inf and tab[0xFC0] == -np.inf
+    pos = tab[:0x7C0]
+    assert pos[0] == 0.0 and np.all(np.diff(pos) > 0)
+    assert np.array_equal(tab[0x800:0x800 + 0x7C0], -pos)
+    assert tab[1] == 2.0 ** -20 and tab[63] == 63 * 2.0 ** -20      # subnormals
+    assert tab[64] == 2.0 ** -14                                    # smallest normal
+    assert tab[15 << 6] == 1.0 and tab[(15 << 6) | 1] == 1.0 + 1 / 64
+    assert tab[0x7BF] == (2 - 1 / 64) * 2.0 ** 15 == 65024.0          # largest finite
+
+
+def test_e5m6_encode_roundtrip_and_every_value_is_bf16():
+    tab = _e5m6_table()
+    for c in list(range(0x7C0)) + list(range(0x800, 0xFC0)):
+        assert oracle.e5m6_encode(tab[c]) == c
+    # every finite E5M6 value is exact in bf16 (6 <= 7 mantissa bits, range inside bf16's)
+    fin = tab[np.isfinite(tab)]
+    b = np.array([oracle.bf16_round(v) for v in fin], np.uint16)
+    assert np.array_equal(np.array([oracle.bf16_value(int(x)) for x in b]), fin)
+
+
+def test_e5m6_encode_exhaustive_bf16_against_linear_scan():
+    """Every finite bf16 value against the nearest of the finite magnitudes
+    and 2^16 (standing for infinity under IEEE overflow), ties to the even
+    code, sign copied."""
+    tab = _e5m6_table()
+    cand = np.concatenate([tab[:0x7C0], [65536.0]])          # codes 0 .. 0x7C0
+    bits = np.arange(65536, dtype=np.uint32)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]
+    vals = (bits << 16).view(np.float32).astype(np.float64)
+    a = np.abs(vals)
+    hi = np.searchsorted(cand, a, side="left").clip(1, len(cand) - 1)
+    lo = hi - 1
+    exact_hi = cand[hi] == a
+    dlo, dhi = a - cand[lo], cand[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(exact_hi, hi, pick)
+    pick = np.where(a >= 65536.0, 0x7C0, pick)
+    want = pick | ((bits >> 15) << 11)
+    got = np.array([oracle.e5m6_encode(v) for v in vals])
+    assert np.array_equal(got, want)
+
+
+def test_e5m6_pack_unpack_rows():
+    """Packed rows (value i in bits 12 i .. 12 i + 11) decode to the values
+    encoded; the packing of a known pair is spelled out."""
+    rng = np.random.default_rng(5)
+    tab = _e5m6_table()
+    codes = rng.integers(0, 4096, (3, 256))
+    codes[~np.isfinite(tab[codes])] = 0x3C0
+    x = np.array([[oracle.bf16_round(tab[c]) for c in row] for row in codes], np.uint16)
+    y = oracle.encode_e5m6(x)
+    assert y.shape == (3, 384)
+    assert np.array_equal(oracle.decode_e5m6(y, 256), x)
+    c0, c1 = int(codes[0, 0]), int(codes[0, 1])
+    assert y[0, 0] == c0 & 0xFF and y[0, 1] == (c0 >> 8) | ((c1 & 0xF) << 4) and y[0, 2] == c1 >> 4
