@@ -131,6 +131,15 @@ fp8bs_status fp8bs_quant_per_tensor(const void* x, int64_t n, uint8_t* q, float*
                                                  static_cast<hipStream_t>(stream)));
 }
 
+fp8bs_status fp8bs_cast_e4m3(const float* x, int64_t n, uint8_t* q, void* stream) {
+  if (n < 0) return FP8BS_ERR_INVALID_ARG;
+  if (n == 0) return FP8BS_OK;
+  if (x == nullptr || q == nullptr) return FP8BS_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(q, 16)) return FP8BS_ERR_MISALIGNED;
+  FP8BS_TRY(check_device());
+  return launched(fp8bs::launch_cast_e4m3(x, n, q, static_cast<hipStream_t>(stream)));
+}
+
 fp8bs_status fp8bs_encode_e5m6(const void* x, int64_t T, int64_t C, int64_t ldx, uint8_t* y,
                                int64_t ldy, void* stream) {
   if (T < 0 || C <= 0) return FP8BS_ERR_INVALID_ARG;

@@ -14,6 +14,8 @@ hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, int64
                                   uint8_t* q, int64_t ldq, float* s, int64_t lds,
                                   hipStream_t st);
 
+hipError_t launch_cast_e4m3(const float* x, int64_t n, uint8_t* q, hipStream_t st);
+
 hipError_t launch_quant_per_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* s,
                                    hipStream_t st);
 

@@ -32,6 +32,7 @@ SRC_FP8_1x128 = 0
 SRC_BF16 = 1
 
 ENTRY_POINTS = ("fp8bs_quant_act_1x128", "fp8bs_quant_w_128x128", "fp8bs_quant_per_tensor",
+                "fp8bs_cast_e4m3",
                 "fp8bs_encode_e5m6", "fp8bs_decode_e5m6", "fp8bs_requant_T_128x1",
                 "fp8bs_transpose_w_128x128", "fp8bs_gemm", "fp8bs_gemm_quant_1x128",
                 "fp8bs_grouped_gemm",
@@ -60,6 +61,7 @@ def load() -> ctypes.CDLL:
         "fp8bs_quant_act_1x128": [P, I64, I64, I64, P, I64, P, I64, P],
         "fp8bs_quant_w_128x128": [P, I64, I64, I64, P, I64, P, I64, P],
         "fp8bs_quant_per_tensor": [P, I64, P, P, P],
+        "fp8bs_cast_e4m3": [P, I64, P, P],
         "fp8bs_encode_e5m6": [P, I64, I64, I64, P, I64, P],
         "fp8bs_decode_e5m6": [P, I64, I64, I64, P, I64, P],
         "fp8bs_requant_T_128x1": [I, P, P, I64, I64, I64, I64, P, I64, P, I64, P],
@@ -136,6 +138,13 @@ def fp8bs_quant_per_tensor(x, q, s, stream=None):
     """x bf16 (contiguous, n % 128 == 0) -> q u8 (same shape), s f32 [1]."""
     assert x.is_contiguous() and q.is_contiguous()
     _call("fp8bs_quant_per_tensor", _ptr(x), x.numel(), _ptr(q), _ptr(s), _stream(stream))
+
+
+def fp8bs_cast_e4m3(x, q, stream=None):
+    """x f32 (contiguous) -> q u8 (same number of elements): nearest-even
+    E4M3 codes, saturated to +-448."""
+    assert x.is_contiguous() and q.is_contiguous() and q.numel() == x.numel()
+    _call("fp8bs_cast_e4m3", _ptr(x), x.numel(), _ptr(q), _stream(stream))
 
 
 def fp8bs_encode_e5m6(x, y, stream=None):

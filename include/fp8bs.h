@@ -105,6 +105,20 @@ fp8bs_status fp8bs_quant_w_128x128(const void *w, int64_t N, int64_t K, int64_t 
 fp8bs_status fp8bs_quant_per_tensor(const void *x, int64_t n, uint8_t *q, float *s, void *stream);
 
 /*
+ * FP32 -> E4M3 codes, nearest-even with saturation: the last step of every
+ * quantizer here ([p1] para 3: a tile, divided by its scaling factor, is
+ * quantized to FP8), run with a unit scale by the same encoder.  For data
+ * whose scale is already applied, and a direct check of the encoder on any
+ * FP32 value.
+ *   x  f32 [n] (contiguous)     q  u8 [n]
+ * q[i] = the E4M3 code nearest to x[i], ties to the even code, |x[i]| > 448
+ * (infinities included) saturated to +-448, the sign of zero kept.  NaN
+ * inputs give an unspecified code.  n >= 0 (0 is a no-op); x and q 16-byte
+ * aligned, else FP8BS_ERR_MISALIGNED.
+ */
+fp8bs_status fp8bs_cast_e4m3(const float *x, int64_t n, uint8_t *q, void *stream);
+
+/*
  * The 12-bit E5M6 format for cached activations.  [p1] para 3: a custom
  * E5M6 format is used for some activations cached for the backward pass.
  * Layout (a reading; the pages give none): bit 11 sign, bits 10..6

@@ -46,6 +46,10 @@ def quant_pt(x=A, n=256, q=A, s=A):
     return fp8bs.load().fp8bs_quant_per_tensor(x, n, q, s, NULL)
 
 
+def cast(x=A, n=100, q=A):
+    return fp8bs.load().fp8bs_cast_e4m3(x, n, q, NULL)
+
+
 def enc6(x=A, T=4, C=128, ldx=128, y=A, ldy=192):
     return fp8bs.load().fp8bs_encode_e5m6(x, T, C, ldx, y, ldy, NULL)
 
@@ -107,6 +111,12 @@ def grouped(a=A, sa=A, ldsa=2, b=A, sb=A, off=A, E=2, M=10, d=A, dt=0, N=128, K=
     (lambda: quant_pt(q=A + 4), fp8bs.ERR_MISALIGNED),
     (lambda: quant_pt(s=A + 2), fp8bs.ERR_MISALIGNED),
     (lambda: quant_pt(n=0, x=NULL, q=NULL, s=NULL), fp8bs.OK),
+    (lambda: cast(n=-1), fp8bs.ERR_INVALID_ARG),
+    (lambda: cast(x=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: cast(q=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: cast(x=A + 4), fp8bs.ERR_MISALIGNED),
+    (lambda: cast(q=A + 8), fp8bs.ERR_MISALIGNED),
+    (lambda: cast(n=0, x=NULL, q=NULL), fp8bs.OK),
     (lambda: enc6(T=-1), fp8bs.ERR_INVALID_ARG),
     (lambda: enc6(C=0), fp8bs.ERR_INVALID_ARG),
     (lambda: enc6(C=64, ldx=64, ldy=96), fp8bs.ERR_UNSUPPORTED_SHAPE),
