@@ -36,6 +36,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+QUEUE_FILL_CYCLES = 4_000_000  # spin before a batch of timed calls (about 2 ms)
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mlp_up_4096x18432x7168_traffic.txt")
 GEMM_SRC = os.path.join(ROOT, "fp8_fine_grained_fp8bs_amd", "csrc", "gemm.hip")
@@ -200,6 +201,10 @@ def time_rows(dev, reps=20, warm=3):
     def timed(name, fn):
         for _ in range(warm):
             fn()
+        # keep the GPU busy while the timed calls are queued, so that the
+        # host's launch latency (longer than the smallest kernels) never
+        # leaves the stream idle between a start event and its kernel
+        torch.cuda._sleep(QUEUE_FILL_CYCLES)
         kt = KernelTimer()
         for _ in range(reps):
             kt.run(name, fn)

@@ -294,7 +294,6 @@ constexpr int kOutFp8 = 2;   // E4M3 codes + one FP32 scale per 1x128 tile along
 
 template <class C, int OUT, bool BROW, bool GROUPED>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
-  constexpr bool OUT_F32 = OUT == kOutF32;
   constexpr int BM = C::BM, BN = C::BN;
   static_assert(C::lds_bytes(BROW) <= 160 * 1024, "LDS budget");
   __shared__ __align__(16) uint8_t lds[C::lds_bytes(BROW)];
