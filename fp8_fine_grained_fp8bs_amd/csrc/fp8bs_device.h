@@ -33,6 +33,7 @@ constexpr float kMarginLo = 1.0f - 0x1p-20f;
 constexpr float kMarginHi = 1.0f + 0x1p-20f;
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
 // 16-byte streaming load (read once: non-temporal hint).
 __device__ __forceinline__ uint4 load16_nt(const void* p) {

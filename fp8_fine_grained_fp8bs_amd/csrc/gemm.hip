@@ -569,7 +569,9 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     // ---- epilogue through stage 2 of the LDS (padded rows, PR rows per
     //      pass), so that every global store writes 16 contiguous bytes per
     //      lane and a wave writes whole output rows.  Lane (fr, kc) holds
-    //      columns 4 kc .. 4 kc + 3 of row fr of each 16x16 block.
+    //      columns 4 kc .. 4 kc + 3 of row fr of each 16x16 block.  The
+    //      stores carry the non-temporal hint: the kernel never reads its
+    //      output, and the caches stay with the operand panels.
     constexpr int OB = OUT == kOutBf16 ? 2 : 4;   // staged bytes per element
     constexpr int ROWB = BN * OB + 16;            // padded LDS row
     constexpr int CPR = BN * OB / 16;             // 16-byte chunks per tile row
@@ -633,7 +635,8 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
           const int64_t m = cm0 + pass * PR + r;
           const int c0 = gc * 128;
           if (m < cm_end && c0 < cols) {
-            *reinterpret_cast<uint2*>(qbase + m * p.ldd + cn0 + c0 + sub * 8) = cw;
+            __builtin_nontemporal_store(u32x2{cw.x, cw.y},
+                                        reinterpret_cast<u32x2*>(qbase + m * p.ldd + cn0 + c0 + sub * 8));
             if (sub == 0) p.s_out[m * p.lds_out + (cn0 + c0) / 128] = ts.s;
           }
         }
@@ -647,7 +650,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
           const uint4 vv = *reinterpret_cast<const uint4*>(ob + r * ROWB + cc * 16);
           uint8_t* dst = dbase + m * ldd_b + (cn0 + c0) * OB;
           if (c0 + 16 / OB <= cols) {
-            *reinterpret_cast<uint4*>(dst) = vv;
+            __builtin_nontemporal_store(u32x4{vv.x, vv.y, vv.z, vv.w}, reinterpret_cast<u32x4*>(dst));
           } else {
             const uint8_t* src = reinterpret_cast<const uint8_t*>(&vv);
             for (int e = 0; e < (cols - c0) * OB; ++e) dst[e] = src[e];
