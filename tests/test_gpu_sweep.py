@@ -1,0 +1,61 @@
+"""Sweeps over the number of 128-wide K groups, G = K / 128, on the GPU
+against the CPU oracle.
+
+The GEMM's main loop is unrolled by 12 groups (stages repeat every 3,
+scale-block quarters every 4) and guards each iteration with g + i < G; its
+scales travel in blocks of 4 groups.  The 1x128 activation quantizer picks
+one of seven kernel shapes from ceil(G / 4) and the row count.  So every
+G from 1 to 26 is run here: all residues of G modulo 12 and 4, with ragged
+M and N, both B-scale modes, FP32 and BF16 outputs; and every G from 1 to
+40 for the activation quantizer, at a row count that takes the persistent
+kernel where it applies.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fp8_fine_grained_fp8bs_amd import fp8bs, synth
+from tests.gpu_common import announce, bf16_dev, check_quant_equal, host, native_loaded
+from tests.test_gpu_gemm import _full_check
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("G", list(range(1, 27)))
+def test_gemm_every_group_count(G):
+    native_loaded()
+    M, N, K = 130, 264, 128 * G
+    q = synth.tiny(M=M, N=N, K=K, seed=100 + G)
+    qa, sa = oracle.quant_act_1x128(q["A"])
+    announce(f"gemm sweep G={G}: {M}x{N}x{K}")
+    if G % 2:
+        qb, sb = oracle.quant_w_128x128(q["W"])
+        _full_check(f"sweep G={G} block", qa, sa, qb, sb, pads=(16, 1, 0, 2, 8))
+    else:
+        qb, sb = oracle.quant_act_1x128(q["W"])
+        _full_check(f"sweep G={G} row", qa, sa, qb, sb, oracle.BSCALE_ROW, pads=(0, 2, 16, 1, 0))
+
+
+@pytest.mark.parametrize("G", list(range(1, 41)))
+def test_quant_act_every_group_count(G):
+    native_loaded()
+    K = 128 * G
+    for M in (33, 1000):
+        x = synth.tiny(M=M, N=1, K=K, seed=200 + G)["A"]
+        announce(f"quant_act sweep G={G}: {M}x{K}")
+        q, s = fp8bs.quant_act_1x128(bf16_dev(x))
+        qr, sr = oracle.quant_act_1x128(x)
+        check_quant_equal(f"quant_act sweep {M}x{K}", host(q), host(s), qr, sr)
+
+
+@pytest.mark.parametrize("M,G", [(11000, 41), (8300, 60)])
+def test_quant_act_row_kernels_on_long_rows(M, G):
+    """Many long rows: the one-wave-per-row kernels with 14 and 16 tile-quads
+    in flight per wave (G = 41: 11 quads; G = 60: 15 quads)."""
+    native_loaded()
+    K = 128 * G
+    x = synth.tiny(M=M, N=1, K=K, seed=300 + G)["A"]
+    announce(f"quant_act long rows: {M}x{K}")
+    q, s = fp8bs.quant_act_1x128(bf16_dev(x))
+    qr, sr = oracle.quant_act_1x128(x)
+    check_quant_equal(f"quant_act long rows {M}x{K}", host(q), host(s), qr, sr)
