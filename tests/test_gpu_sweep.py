@@ -59,3 +59,51 @@ def test_quant_act_row_kernels_on_long_rows(M, G):
     q, s = fp8bs.quant_act_1x128(bf16_dev(x))
     qr, sr = oracle.quant_act_1x128(x)
     check_quant_equal(f"quant_act long rows {M}x{K}", host(q), host(s), qr, sr)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_grouped_random_expert_counts(case):
+    """Seeded random expert counts (empty experts, counts below, at and just
+    past a 128-row tile), expert counts 1 .. 16, several K and N: every
+    output entry against the oracle."""
+    from tests.gpu_common import check_bf16_is_rounded_f32, check_f32_gemm
+    from tests.test_gpu_gemm import _grouped_dev
+    native_loaded()
+    rng = np.random.default_rng(400 + case)
+    E = int(rng.choice([1, 2, 3, 5, 8, 16]))
+    counts = rng.choice([0, 1, 5, 127, 128, 129, 200, 256, 300], size=E)
+    if counts.sum() == 0:
+        counts[0] = 129
+    N = int(rng.choice([128, 256, 384]))
+    K = 128 * int(rng.integers(1, 15))
+    off = synth.offsets_from_counts(counts)
+    T = int(off[-1])
+    x = synth.tiny(M=T, N=1, K=K, seed=500 + case)["A"]
+    w = synth.tiny(M=1, N=E * N, K=K, seed=600 + case)["W"]
+    qa, sa = oracle.quant_act_1x128(x)
+    qb, sb = oracle.quant_w_128x128(w)
+    qb = qb.reshape(E, N, K); sb = sb.reshape(E, N // 128, K // 128)
+    announce(f"grouped sweep {case}: E={E} counts={counts.tolist()} N={N} K={K}")
+    ref = oracle.grouped_gemm(qa, sa, qb, sb, off)
+    mag = oracle.grouped_gemm(qa & 0x7F, np.abs(sa), qb & 0x7F, np.abs(sb), off)
+    d32 = host(_grouped_dev(qa, sa, qb, sb, off, True))
+    check_f32_gemm(f"grouped sweep {case} f32", d32, ref, mag)
+    d16 = host(_grouped_dev(qa, sa, qb, sb, off, False))
+    check_bf16_is_rounded_f32(f"grouped sweep {case} bf16", d16, d32)
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 5, 11, 12, 13, 25])
+def test_gemm_quant_closed_form_group_counts(G):
+    """The fused output quantization over several K-group counts, on
+    operands whose FP32 result is exact: codes and scales bit-exact."""
+    from tests.test_gpu_gemm_quant import _gemm_quant_dev
+    from tests.test_oracle_gemm import quant_output_closed_form_case
+    native_loaded()
+    rng = np.random.default_rng(700 + G)
+    a, sa, b, sbb, sbr, q_exp, s_exp = quant_output_closed_form_case(rng, 70, 384, G=G)
+    for sb, mode in ((sbb, fp8bs.BSCALE_BLOCK_128x128), (sbr, fp8bs.BSCALE_ROW_1x128)):
+        announce(f"gemm_quant closed form G={G} bmode {mode}")
+        q_ref, s_ref = oracle.gemm_quant_1x128(a, sa, b, sb, mode)
+        assert np.array_equal(q_ref, q_exp) and np.array_equal(s_ref, s_exp)
+        q, s = _gemm_quant_dev(a, sa, b, sb, mode, pad_q=16, pad_s=1)
+        check_quant_equal(f"gemm_quant closed form G={G}", q, s, q_ref, s_ref)

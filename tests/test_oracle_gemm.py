@@ -98,30 +98,40 @@ def test_input_gradient_through_transposed_weight_equals_int_matmul():
     assert np.array_equal(d, ref)
 
 
-def quant_output_closed_form_case(rng, M, N, pow2_range=(-20, 20)):
-    """Operands whose GEMM result is known in closed form: a[m] = 1.0 at
-    k = 0 with sa[m] = t_m (a power of two), b[n] = code c_n at k = 0 with
-    unit scales, so D[m][n] = t_m * dec(c_n) exactly.  Every 128-column
-    group holds a 448 code, so each output tile's scale is t_m and its codes
-    are the c_n.  Returns (a, sa, b, sb_block, sb_row, expected codes,
-    expected scales)."""
-    K = 128
+def quant_output_closed_form_case(rng, M, N, pow2_range=(-20, 20), G=1):
+    """Operands whose GEMM result is known in closed form: row m of A holds
+    1.0 at the first k of one K group g_m (group 0 when G = 1) with
+    sa[m][g_m] = t_m (a power of two) and zero codes elsewhere; every K group
+    of B row n starts with code c_n, all B scales are 1.  So D[m][n] =
+    t_m * dec(c_n) exactly.  Every 128-column group holds a 448 code, so each
+    output tile's scale is t_m and its codes are the c_n.  Returns (a, sa, b,
+    sb_block, sb_row, expected codes, expected scales)."""
+    K = 128 * G
     c = rng.integers(0, 256, N).astype(np.uint8)
     c[(c & 0x7F) == 0x7F] = 0x3C
     c[c == 0x80] = 0x00           # a sum starting from +0 cannot give -0
     c[::128] = 0x7E | (rng.integers(0, 2, len(c[::128])) << 7).astype(np.uint8)
     t = (2.0 ** rng.integers(*pow2_range, M)).astype(np.float32)
-    a = np.zeros((M, K), np.uint8); a[:, 0] = 0x38
-    b = np.zeros((N, K), np.uint8); b[:, 0] = c
-    sa = t.reshape(M, 1)
-    sb_block = np.ones(((N + 127) // 128, 1), np.float32)
-    sb_row = np.ones((N, 1), np.float32)
+    gsel = rng.integers(0, G, M) if G > 1 else np.zeros(M, np.int64)
+    a = np.zeros((M, K), np.uint8); a[np.arange(M), 128 * gsel] = 0x38
+    b = np.zeros((N, K), np.uint8); b[:, ::128] = c.reshape(N, 1)
+    sa = np.ones((M, G), np.float32); sa[np.arange(M), gsel] = t
+    sb_block = np.ones(((N + 127) // 128, G), np.float32)
+    sb_row = np.ones((N, G), np.float32)
     return a, sa, b, sb_block, sb_row, np.tile(c, (M, 1)), np.repeat(t.reshape(M, 1), N // 128, 1)
 
 
 def test_gemm_quant_1x128_closed_form():
     rng = np.random.default_rng(8)
     a, sa, b, sbb, sbr, q_exp, s_exp = quant_output_closed_form_case(rng, 40, 384)
+    for sb, mode in ((sbb, oracle.BSCALE_BLOCK), (sbr, oracle.BSCALE_ROW)):
+        q, s = oracle.gemm_quant_1x128(a, sa, b, sb, mode)
+        assert np.array_equal(s, s_exp) and np.array_equal(q, q_exp)
+
+
+def test_gemm_quant_1x128_closed_form_several_groups():
+    rng = np.random.default_rng(10)
+    a, sa, b, sbb, sbr, q_exp, s_exp = quant_output_closed_form_case(rng, 20, 256, G=5)
     for sb, mode in ((sbb, oracle.BSCALE_BLOCK), (sbr, oracle.BSCALE_ROW)):
         q, s = oracle.gemm_quant_1x128(a, sa, b, sb, mode)
         assert np.array_equal(s, s_exp) and np.array_equal(q, q_exp)
