@@ -84,9 +84,8 @@ def test_encode_exhaustive_bf16_against_linear_scan():
     """Every finite bf16 pattern (scale 1) against nearest-by-scan over the
     PyTorch value table."""
     bits = np.arange(65536, dtype=np.uint32)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]   # finite patterns only
     vals = (bits << 16).view(np.float32).astype(np.float64)
-    fin = np.isfinite(vals)
-    vals = vals[fin]
     tab = torch_e4m3_table()[:127]            # non-negative finite magnitudes
     a = np.minimum(np.abs(vals), tab.max())
     d = np.abs(a[:, None] - tab[None, :])
