@@ -87,11 +87,15 @@ def status_string(st: int) -> str:
 
 
 def _ptr(t):
-    """Device pointer of a tensor (or an int address, or None for NULL)."""
+    """Device pointer of a GPU tensor (or an int address, or None for NULL).
+    A host tensor is refused here: its address would reach the kernels as a
+    device pointer."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError("libfp8bs takes device tensors; got a tensor on " + str(t.device))
     return t.data_ptr()
 
 

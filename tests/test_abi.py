@@ -215,6 +215,7 @@ def test_valid_call_without_gpu_reports_no_device():
 def test_python_binding_raises_on_error():
     class Fake:
         shape = (4, 100)
+        is_cuda = True
         def data_ptr(self):
             return A
         def stride(self, i):
@@ -224,3 +225,13 @@ def test_python_binding_raises_on_error():
     with pytest.raises(fp8bs.Fp8bsError) as ei:
         fp8bs.fp8bs_quant_act_1x128(Fake(), Fake(), Fake(), stream=0)
     assert ei.value.status == fp8bs.ERR_UNSUPPORTED_SHAPE
+
+
+def test_binding_refuses_host_tensors():
+    """A CPU tensor's address must never reach a kernel as a device pointer."""
+    import torch
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)
+    q = torch.zeros((4, 128), dtype=torch.uint8)
+    s = torch.zeros((4, 1), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        fp8bs.fp8bs_quant_act_1x128(x, q, s, stream=0)
