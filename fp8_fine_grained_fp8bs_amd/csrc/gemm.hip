@@ -41,9 +41,10 @@
 //   groups of one row, so a row's scales cost one cache line per 4 groups
 //   instead of one per group.
 // * Tiles are handed out XCD-aware: the 8 XCDs each take a contiguous range
-//   of the tile order, and the order walks 4 M-tiles x all N-tiles per
-//   group, so the ~32 workgroups resident on one XCD share A and B panels
-//   in that XCD's L2.
+//   of the tile order, and the order walks 8 M-tiles x all N-tiles per
+//   group, so the ~32 workgroups resident on one XCD (8 M-tiles x 4 N-tiles
+//   at a time: the B panel of a 128x256 tile is twice the A panel) share A
+//   and B panels in that XCD's L2.
 // * Workgroups are persistent (one per compute unit): after a tile's last
 //   K group the first K groups of the workgroup's next tile are copied while
 //   the finished tile goes out through LDS with 16-byte stores, as BF16,
@@ -60,7 +61,7 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) int v8i;
 typedef __attribute__((ext_vector_type(4))) float v4f;
 
-constexpr int GROUP_M = 4;     // M-tiles per group of the tile order
+constexpr int GROUP_M = 8;     // M-tiles per group of the tile order
 constexpr int NUM_XCD = 8;
 constexpr int SBLK = 4;        // K groups per scale block
 constexpr int NSLOT = 3;       // scale blocks resident in LDS
