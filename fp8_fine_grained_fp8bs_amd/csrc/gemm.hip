@@ -61,7 +61,8 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) int v8i;
 typedef __attribute__((ext_vector_type(4))) float v4f;
 
-constexpr int GROUP_M = 8;     // M-tiles per group of the tile order
+constexpr int GROUP_M = 8;          // M-tiles per group of the tile order
+constexpr int GROUP_M_EXPERTS = 4;  // the same for the grouped form (see tile_of)
 constexpr int NUM_XCD = 8;
 constexpr int SBLK = 4;        // K groups per scale block
 constexpr int NSLOT = 3;       // scale blocks resident in LDS
@@ -125,15 +126,19 @@ __device__ __forceinline__ v4f mfma_16x16x128_fp8(const v8i& a, const v8i& b) {
 // Byte offset of logical 16-byte chunk `ch` of tile row `r` in LDS.
 __device__ __forceinline__ int swz(int r, int ch) { return r * 128 + ((ch ^ ((r >> 1) & 7)) << 4); }
 
-// Workgroup id -> tile, XCD-aware (see the header comment).
+// Workgroup id -> tile, XCD-aware (see the header comment).  In the grouped
+// form every expert has its own B, so a group of M-tiles that spans two
+// experts needs both experts' B panels: smaller groups cross fewer expert
+// boundaries (measured 5% faster with 4 than with 8 on the MoE shapes).
+template <int GM>
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& vm, int& nt) {
   const int total = tiles_m * tiles_n;
   const int q = total / NUM_XCD, r = total % NUM_XCD;
   const int x = bid % NUM_XCD, local = bid / NUM_XCD;
   const int t = x * q + (x < r ? x : r) + local;
-  const int group = GROUP_M * tiles_n;
-  const int first_m = (t / group) * GROUP_M;
-  const int gm = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
+  const int group = GM * tiles_n;
+  const int first_m = (t / group) * GM;
+  const int gm = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
   const int rr = t % group;
   vm = first_m + rr % gm;
   nt = rr / gm;
@@ -316,7 +321,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   const int vtiles = p.tiles_m * p.tiles_n;
   auto plan_tile = [&](int v) -> bool {
     int vm, nt;
-    tile_of(v, p.tiles_m, p.tiles_n, vm, nt);
+    tile_of<GROUPED ? GROUP_M_EXPERTS : GROUP_M>(v, p.tiles_m, p.tiles_n, vm, nt);
     n0 = static_cast<int64_t>(nt) * BN;
     if (GROUPED) {
       int64_t mt = vm;
