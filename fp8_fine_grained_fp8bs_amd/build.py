@@ -20,7 +20,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8bs.so")
+# debug build for race checks: kernels fill their LDS with 0xFF before use
+POISON_LIB = os.path.join(PKG, "libfp8bs_poison.so")
 SOURCES = ["api.hip", "quant.hip", "requant.hip", "gemm.hip", "e5m6.hip"]
+LDS_SOURCES = ["quant.hip", "requant.hip", "gemm.hip"]   # the sources whose kernels use LDS
 ARCH = "gfx950"
 
 
@@ -38,10 +41,11 @@ def common_flags():
             "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-result"]
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, poison: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ("_poison.o" if poison else ".o"))
+    extra = ["-DFP8BS_POISON_LDS"] if poison else []
+    cmd = [hipcc()] + common_flags() + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -51,18 +55,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libfp8bs.so next to this file."""
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link libfp8bs.so next to this file, and
+    the LDS-poisoning debug build libfp8bs_poison.so (tests only)."""
+    jobs = [(src, False) for src in SOURCES] + [(src, True) for src in LDS_SOURCES]
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    plain = dict(zip(SOURCES, objs[:len(SOURCES)]))
+    poisoned = dict(zip(LDS_SOURCES, objs[len(SOURCES):]))
+    _link([plain[s] for s in SOURCES], LIB)
+    _link([poisoned.get(s, plain[s]) for s in SOURCES], POISON_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", POISON_LIB)
     return LIB
 
 

@@ -157,6 +157,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
 }
 
+// Debug builds with FP8BS_POISON_LDS fill a kernel's LDS with 0xFF bytes
+// (NaN as FP32, and the NaN code as E4M3) before its first use, so that a
+// read of LDS that the kernel never wrote changes its results.  Called at
+// the top of a kernel by every thread; a no-op in the library build.
+template <int BYTES>
+__device__ __forceinline__ void poison_lds(void* lds) {
+#ifdef FP8BS_POISON_LDS
+  uint32_t* p = static_cast<uint32_t*>(lds);
+  for (int i = static_cast<int>(threadIdx.x); i < BYTES / 4; i += static_cast<int>(blockDim.x))
+    p[i] = 0xffffffffu;
+  __syncthreads();
+#else
+  (void)lds;
+#endif
+}
+
 // Direct global -> LDS copies through buffer descriptors.
 // buffer_load_dword{,x4} ... offen lds writes lane l's 4 (16) bytes at
 // M0 + 4 l (16 l).  The descriptor covers only the valid rows of the tile:

@@ -303,6 +303,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   constexpr int BM = C::BM, BN = C::BN;
   static_assert(C::lds_bytes(BROW) <= 160 * 1024, "LDS budget");
   __shared__ __align__(16) uint8_t lds[C::lds_bytes(BROW)];
+  poison_lds<C::lds_bytes(BROW)>(lds);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -158,6 +158,7 @@ __global__ __launch_bounds__(256) void quant_w_kernel(const uint16_t* __restrict
                                                       int64_t ldq, float* __restrict__ s,
                                                       int64_t lds) {
   __shared__ float wave_amax[4];
+  poison_lds<sizeof(wave_amax)>(wave_amax);
   const int g = blockIdx.x;
   const int64_t nb = blockIdx.y;
   const int tid = threadIdx.x;

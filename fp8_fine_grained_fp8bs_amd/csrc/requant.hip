@@ -47,6 +47,8 @@ __global__ __launch_bounds__(256) void requant_kernel(const uint8_t* __restrict_
   constexpr int CPT = SRC_BF16 ? 2 : 4;     // channels per thread
   __shared__ __align__(16) uint8_t tile[2][128 * 128];
   __shared__ float srow[2][128];
+  poison_lds<sizeof(tile)>(tile);
+  poison_lds<sizeof(srow)>(srow);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -179,6 +181,7 @@ __global__ __launch_bounds__(256) void transpose_w_kernel(const uint8_t* __restr
                                                           float* __restrict__ st, int64_t ldst,
                                                           int64_t tiles, int64_t ktiles) {
   __shared__ __align__(16) uint8_t tile[2][128 * 128];
+  poison_lds<sizeof(tile)>(tile);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -39,6 +39,17 @@ ENTRY_POINTS = ("fp8bs_quant_act_1x128", "fp8bs_quant_w_128x128", "fp8bs_quant_p
                 "fp8bs_status_string", "fp8bs_version")
 
 _lib = None
+_lib_path = LIB_PATH
+
+
+def use_library(path: str) -> str:
+    """Route every later call through another build of the library (the
+    tests use the LDS-poisoning debug build, ``libfp8bs_poison.so``);
+    returns the path in use before."""
+    global _lib, _lib_path
+    prev = _lib_path
+    _lib_path, _lib = path, None
+    return prev
 
 
 class Fp8bsError(RuntimeError):
@@ -52,10 +63,10 @@ def load() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+    if not os.path.exists(_lib_path):
+        raise RuntimeError(f"{_lib_path} is missing: build it with "
                            "`python -m fp8_fine_grained_fp8bs_amd.build` (hipcc, gfx950)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(_lib_path)
     P, I64, I32, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
     sigs = {
         "fp8bs_quant_act_1x128": [P, I64, I64, I64, P, I64, P, I64, P],
