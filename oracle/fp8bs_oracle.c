@@ -73,17 +73,14 @@ double orc_e4m3_value(uint8_t code)
 }
 
 /* Magnitude table of the 127 non-negative finite codes 0x00..0x7E.  The
- * codes are ordered by value, so index == code. */
+ * codes are ordered by value, so index == code.  Filled once when the
+ * library is loaded, before any (parallel) caller can use it. */
 static double g_mag[127];
-static int g_mag_ready = 0;
 
-static void build_mag_table(void)
+__attribute__((constructor)) static void build_mag_table(void)
 {
-    if (g_mag_ready)
-        return;
     for (int c = 0; c < 127; ++c)
         g_mag[c] = orc_e4m3_value((uint8_t)c);
-    g_mag_ready = 1;
 }
 
 /* Round a finite binary64 value to the nearest E4M3 code, ties to the code
@@ -92,7 +89,6 @@ static void build_mag_table(void)
  * then compare against their exact midpoint. */
 uint8_t orc_e4m3_encode(double y)
 {
-    build_mag_table();
     uint8_t sign = signbit(y) ? 0x80 : 0x00;
     double a = fabs(y);
     if (a >= g_mag[126])
@@ -541,15 +537,15 @@ double orc_e5m6_value(uint16_t code)
  * ordered table of the 1984 non-negative finite magnitudes (codes 0..0x7BF
  * are ordered by value). */
 static double g_m6[1984];
-static int g_m6_ready = 0;
+
+__attribute__((constructor)) static void build_m6_table(void)
+{
+    for (int c = 0; c < 1984; ++c)
+        g_m6[c] = orc_e5m6_value((uint16_t)c);
+}
 
 uint16_t orc_e5m6_encode(double y)
 {
-    if (!g_m6_ready) {
-        for (int c = 0; c < 1984; ++c)
-            g_m6[c] = orc_e5m6_value((uint16_t)c);
-        g_m6_ready = 1;
-    }
     uint16_t sign = signbit(y) ? 0x800 : 0;
     double a = fabs(y);
     double top = g_m6[1983];
