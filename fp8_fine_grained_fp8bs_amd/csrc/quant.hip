@@ -232,7 +232,8 @@ __global__ __launch_bounds__(256) void cast_e4m3_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------
-// Per-tensor scaling, the practice [p3] para 4 describes (the tensor's
+// Per-tensor scaling, the practice that [p3] para 4
+// (xn--9g3bo1gtkw0l8ubf92bgle.kr post wr_id=113503) describes (the tensor's
 // max-abs mapped to the FP8 maximum) and [p1] para 4 contrasts with the
 // fine-grained tiles; kept as the comparison path of the accuracy study.
 // Three passes over a contiguous bf16 tensor whose length is a multiple of

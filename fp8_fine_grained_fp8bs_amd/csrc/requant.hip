@@ -150,8 +150,9 @@ __global__ __launch_bounds__(256) void requant_kernel(const uint8_t* __restrict_
 
 // ---------------------------------------------------------------------
 // Transpose of 128x128-block-quantized weights, for the backward pass for
-// the input ([p3] para 4 splits the backward pass into a part for the
-// input and a part for the weights).  dX = dY W consumes W as the B
+// the input ([p3] para 4, xn--9g3bo1gtkw0l8ubf92bgle.kr post wr_id=113503,
+// splits the backward pass into a part for the input and a part for the
+// weights).  dX = dY W consumes W as the B
 // operand of a K-contiguous GEMM, i.e. as W^T [K][N].  The max-abs of a
 // 128x128 block does not depend on its orientation, so the blocks of W^T
 // are the transposed blocks of W with the same scales: the codes move as

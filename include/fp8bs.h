@@ -6,6 +6,7 @@
  * excerpts on five web pages, cited as
  *   [p1] xn--9g3bo1gtkw0l8ubf92bgle.kr board post wr_id=32373
  *   [p2] why-be.why-be.co.kr board post wr_id=73620
+ *   [p3] xn--9g3bo1gtkw0l8ubf92bgle.kr board post wr_id=113503
  *   [p4] bestpmk.kr board post wr_id=299512
  * with a paragraph number counted on that page.
  *
