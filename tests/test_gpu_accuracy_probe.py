@@ -8,7 +8,7 @@ unquantized binary64 GEMM of the bf16 inputs, next to two references:
 * a BF16 GEMM with an FP32 accumulator and BF16 output.
 
 The report's context figure for the unpromoted case is a maximum relative
-error of nearly 2 % at K = 4096 ([p1] = xn--9g3bo1gtkw0l8ubf92bgle.kr post
+error of about 2 % at K = 4096 ([p1] = xn--9g3bo1gtkw0l8ubf92bgle.kr post
 wr_id=32373, paragraph 4).  The test prints the table and checks the
 ordering the method relies on: promotion keeps the FP8 GEMM's error at the
 level of its quantization error, far below the unpromoted model's.
@@ -81,7 +81,7 @@ def test_accuracy_probe_k4096():
     pt = total_table["fine-grained FP8, promoted (GPU)"]
     bt = total_table["BF16 GEMM (FP32 accumulate, BF16 out)"]
     # promotion keeps accumulation error orders of magnitude below the
-    # unpromoted model (whose level is the report's "nearly 2 %" context)
+    # unpromoted model (whose level is the report's context figure of about 2 %)
     assert pa["max|err|/max|ref|"] < 1e-3
     assert ua["max|err|/max|ref|"] > 100 * pa["max|err|/max|ref|"]
     # the promoted FP8 GEMM's total error is its quantization error
