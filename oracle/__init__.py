@@ -13,9 +13,11 @@ wr_id=32373, [p2] = why-be.why-be.co.kr post wr_id=73620, [p3] =
 xn--9g3bo1gtkw0l8ubf92bgle.kr post wr_id=113503, [p4] = bestpmk.kr post
 wr_id=299512, with a paragraph number) that it follows.
 
-Parity status: every function below is pinned by ``tests/test_oracle_*.py``
-except :func:`gemm_unpromoted` (the limited-precision accumulation model,
-context only), which is "parity unpinned".
+Parity status: every function below is pinned by ``tests/test_oracle_*.py``.
+The limited-precision accumulation model (:func:`gemm_unpromoted`, context
+only) is pinned by hand-worked cases (``tests/golden/unpromoted_hand.json``)
+that fix its window, truncation direction, chunk boundary, carried sum and
+scale placement, and by the exact sum it reduces to with a wide window.
 """
 from __future__ import annotations
 
@@ -368,7 +370,8 @@ def gemm_bf16_f32acc(x, w) -> np.ndarray:
 def gemm_unpromoted(a, sa_t: float, b, sb_t: float, chunk: int = 32,
                     bits: int = 14) -> np.ndarray:
     """Limited-precision accumulation model without promotion ([p1] para 3,
-    [p2] para 3).  Parity unpinned: context only."""
+    [p2] para 3).  Context only (not the GPU path's reference); pinned by
+    hand-worked cases."""
     a = _u8(a); b = _u8(b)
     M, K = a.shape
     N = b.shape[0]

@@ -443,8 +443,9 @@ void orc_gemm_bf16_f32acc(const uint16_t *x, const uint16_t *w, int64_t M,
 /* Limited-precision accumulation without promotion, after the H800
  * description ([p1] para 3: about 14 retained bits; [p2] para 3: only the
  * top 14 bits of each mantissa product survive, after a sign-filling right
- * shift, lower bits are truncated).  Reading adopted (parity unpinned,
- * context only): per-tensor scales sa_t, sb_t; the K products of the raw
+ * shift, lower bits are truncated).  Reading adopted (context only; pinned
+ * by hand-worked cases in tests/golden/unpromoted_hand.json): per-tensor
+ * scales sa_t, sb_t; the K products of the raw
  * E4M3 codes are taken in chunks of `chunk` products; for each chunk, the
  * running accumulator and the chunk's products are aligned to the largest
  * exponent among them, each is truncated toward minus infinity to `bits`

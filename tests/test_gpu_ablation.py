@@ -1,8 +1,8 @@
 """Accuracy ablation on outlier data: fine-grained scaling (1x128 activation
 tiles, 128x128 weight blocks) against per-tensor scaling, both run on the GPU
 (quantizers and block-scaled GEMM), next to the CPU model of unpromoted
-limited-precision accumulation on the per-tensor codes (context only, parity
-unpinned) and a BF16 GEMM with FP32 accumulation.  Every error is taken
+limited-precision accumulation on the per-tensor codes (context only, pinned
+by hand-worked cases) and a BF16 GEMM with FP32 accumulation.  Every error is taken
 against the binary64 GEMM of the unquantized bf16 inputs.
 
 Data: the small configuration (1% of A's entries x50), 256 rows of the

@@ -4,7 +4,7 @@ unquantized binary64 GEMM of the bf16 inputs, next to two references:
 
 * the limited-precision accumulation model without promotion on per-tensor
   scaled FP8 operands (the behaviour the report attributes to H800 Tensor
-  Cores; parity unpinned, context only), and
+  Cores; context only; pinned by hand-worked cases), and
 * a BF16 GEMM with an FP32 accumulator and BF16 output.
 
 The report's context figure for the unpromoted case is a maximum relative

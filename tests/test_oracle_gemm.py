@@ -217,3 +217,80 @@ def test_bf16_gemm_references():
     m, n = 3, 5
     exact = sum(Fraction(float(xa[m, k])) * Fraction(float(xw[n, k])) for k in range(256))
     assert abs(Fraction(d64[m, n]) - exact) <= 512 * Fraction(2) ** -53 * Fraction(mag[m, n])
+
+
+def _unpromoted_case_operands(case):
+    a = _rle(case["a"])
+    b = _rle(case["b"]) if "b" in case else np.full(a.size, 0x38, np.uint8)
+    assert a.size == b.size
+    return a[None, :], b[None, :]
+
+
+def test_unpromoted_hand_cases():
+    """The limited-precision accumulation model against hand-worked cases:
+    window position (14 bits below the chunk's leading bit), truncation
+    toward minus infinity, the carried sum inside the alignment, the
+    32-product chunk boundary and the place of the per-tensor scales."""
+    cases = json.load(open(os.path.join(GOLDEN, "unpromoted_hand.json")))["cases"]
+    for case in cases:
+        a, b = _unpromoted_case_operands(case)
+        d = oracle.gemm_unpromoted(a, case["sa"], b, case["sb"])
+        assert d.shape == (1, 1)
+        assert d[0, 0] == case["d"], (case["note"], d[0, 0])
+
+
+def test_unpromoted_parameters_move_the_window():
+    """The alternative values stated in the hand cases' notes: one bit more
+    or fewer, and a chunk boundary one product off."""
+    cases = {c["note"].split(":")[0]: c for c in
+             json.load(open(os.path.join(GOLDEN, "unpromoted_hand.json")))["cases"]}
+
+    def run(prefix, **kw):
+        c = next(v for k, v in cases.items() if k.startswith(prefix))
+        a, b = _unpromoted_case_operands(c)
+        return oracle.gemm_unpromoted(a, c["sa"], b, c["sb"], **kw)[0, 0]
+
+    assert run("a product equal to the last kept bit", bits=13) == 448.0
+    assert run("a product one bit below", bits=15) == 448.015625
+    assert run("chunk boundary after 32 products", chunk=33) == 448.0
+    assert run("chunk boundary after 32 products", chunk=31) == 448.03125
+    assert run("the running sum joins", chunk=64) == 448.0
+    assert run("a product below the 14-bit window", bits=24) == 448.0 + 31 * 2.0 ** -9
+
+
+def test_unpromoted_wide_window_is_the_exact_sum():
+    """With 53 kept bits nothing is truncated (products are multiples of
+    2^-18 below 2^18 and the sums stay below 2^26), so the model equals
+    the exact sum of the code products times the per-tensor scales."""
+    rng = np.random.default_rng(21)
+    M, N, K = 3, 4, 200
+    a = _rand_codes(rng, (M, K))
+    b = _rand_codes(rng, (N, K))
+    sa, sb = 0.25, 2.0
+    d = oracle.gemm_unpromoted(a, sa, b, sb, chunk=32, bits=53)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(Fraction(float(TAB[a[m, k]])) * Fraction(float(TAB[b[n, k]])) for k in range(K))
+            assert Fraction(d[m, n]) == exact * Fraction(sa) * Fraction(sb)
+    # and with 14 bits the model loses something on the same data
+    d14 = oracle.gemm_unpromoted(a, sa, b, sb)
+    assert not np.array_equal(d14, d)
+
+
+def test_bf16_f32acc_sums_in_binary32_in_k_order():
+    """The FP32-accumulating BF16 GEMM: products 1, 2^-24, 2^-24 summed in
+    binary32 with k ascending stay at 1 (each addition is a tie that rounds
+    to even); binary64 would give 1 + 2^-23.  The reversed order sums the
+    two small products first and reaches 1 + 2^-23 exactly."""
+    one, tiny = 0x3F80, 0x3980        # bf16 bit patterns of 1.0 and 2^-12
+    x = np.array([[one, tiny, tiny], [tiny, tiny, one]], np.uint16)
+    w = np.array([[one, tiny, tiny], [one, tiny, tiny]], np.uint16)
+    d = oracle.gemm_bf16_f32acc(x, w)
+    assert d.dtype == np.float32
+    assert d[0, 0] == np.float32(1.0)
+    # row 1 against row 0 of w: products 2^-12, 2^-24, 2^-12 (exact in binary32)
+    assert d[1, 0] == np.float32(2.0 ** -11 + 2.0 ** -24)
+    x2 = np.array([[tiny, tiny, one]], np.uint16)
+    w2 = np.array([[tiny, tiny, one]], np.uint16)
+    assert oracle.gemm_bf16_f32acc(x2, w2)[0, 0] == np.float32(1.0 + 2.0 ** -23)
+    assert oracle.gemm_bf16_f64(x, w)[0, 0] == 1.0 + 2.0 ** -23
