@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 QUEUE_FILL_CYCLES = 4_000_000  # spin before a batch of timed calls (about 2 ms)
+FLUSH_BYTES = 1 << 30          # cache flush written between timed row calls
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mlp_up_4096x18432x7168_traffic.txt")
 GEMM_SRC = os.path.join(ROOT, "fp8_fine_grained_fp8bs_amd", "csrc", "gemm.hip")
@@ -66,7 +67,8 @@ def bf16_dev(a, dev):
 
 
 class KernelTimer:
-    """Per-kernel HIP-event timing on the current stream."""
+    """Per-kernel HIP-event timing on the current stream (the stream every
+    library call here is launched on)."""
 
     def __init__(self):
         self.events = {}
@@ -79,12 +81,38 @@ class KernelTimer:
         e.record()
         self.events.setdefault(name, []).append((s, e))
 
+    def times_ms(self, name):
+        return [s.elapsed_time(e) for s, e in self.events[name]]
+
     def mean_ms(self, name):
-        ev = self.events[name]
-        return sum(s.elapsed_time(e) for s, e in ev) / len(ev)
+        t = self.times_ms(name)
+        return sum(t) / len(t)
+
+    def stats_us(self, name):
+        """mean, median and min of the recorded calls, in microseconds."""
+        t = sorted(self.times_ms(name))
+        n = len(t)
+        med = t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
+        return {"us": sum(t) / n * 1e3, "us_median": med * 1e3, "us_min": t[0] * 1e3, "calls": n}
 
     def reset(self):
         self.events = {}
+
+
+class CacheFlush:
+    """Writes FLUSH_BYTES (more than the 256 MB MALL and all L2s together,
+    four times over) on the current stream, so that a following kernel
+    finds none of its inputs in any cache.  Run between timed calls,
+    outside their events."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(self.n & 0xFF)
 
 
 def gemm_source_hash():
@@ -180,11 +208,15 @@ def time_fused(dev, qx, sx, qw, sw, Y, reps=20, warm=3):
     fl = 2.0 * M * N * K
     ms_f = kt.mean_ms("fused")
     ms_u = kt.mean_ms("u_gemm") + kt.mean_ms("u_quant")
+    sf, sg, sq = kt.stats_us("fused"), kt.stats_us("u_gemm"), kt.stats_us("u_quant")
     return {
         "gemm_quant_1x128": {"shape": f"M{M} N{N} K{K}, E4M3 out + 1x128 scales", "us": ms_f * 1e3,
-                             "TFLOP/s": fl / ms_f / 1e9, "frac_fp8_peak": fl / ms_f / 1e9 / FP8_PEAK_TFLOPS},
+                             "us_median": sf["us_median"], "us_min": sf["us_min"],
+                             "TFLOP/s": fl / ms_f / 1e9, "frac_fp8_peak": fl / ms_f / 1e9 / FP8_PEAK_TFLOPS,
+                             "timing": "alternating with the unfused pair, no flush (each launch streams > 1 GB)"},
         "gemm_bf16_then_quant_act": {"shape": f"M{M} N{N} K{K}, BF16 out, then quant_act of [{M}][{N}]",
-                                     "us": ms_u * 1e3, "TFLOP/s": fl / ms_u / 1e9,
+                                     "us": ms_u * 1e3, "us_median": sg["us_median"] + sq["us_median"],
+                                     "TFLOP/s": fl / ms_u / 1e9,
                                      "frac_fp8_peak": fl / ms_u / 1e9 / FP8_PEAK_TFLOPS,
                                      "quant_act_us": kt.mean_ms("u_quant") * 1e3},
     }
@@ -197,8 +229,12 @@ def time_rows(dev, reps=20, warm=3):
     import torch
     from fp8_fine_grained_fp8bs_amd import fp8bs, synth
     rows = {}
+    flush = CacheFlush(dev)
+    stats = {}
 
     def timed(name, fn):
+        """Median event time (ms) of `reps` calls, each after a 1 GiB cache
+        flush written outside its events; mean, median and min kept."""
         for _ in range(warm):
             fn()
         # keep the GPU busy while the timed calls are queued, so that the
@@ -207,9 +243,11 @@ def time_rows(dev, reps=20, warm=3):
         torch.cuda._sleep(QUEUE_FILL_CYCLES)
         kt = KernelTimer()
         for _ in range(reps):
+            flush()
             kt.run(name, fn)
         torch.cuda.synchronize()
-        return kt.mean_ms(name)
+        stats[name] = kt.stats_us(name)
+        return stats[name]["us_median"] * 1e-3
 
     # backward wgrad: X 8192x7168, dY 8192x2048
     log("rows: wgrad inputs")
@@ -298,6 +336,18 @@ def time_rows(dev, reps=20, warm=3):
         rows[f"grouped_gemm_{tag}"] = {"shape": f"E{E} sumM{Ttok} N{N} K{K}", "us": ms * 1e3,
                                        "TFLOP/s": fl / ms / 1e9, "frac_fp8_peak": fl / ms / 1e9 / FP8_PEAK_TFLOPS}
         del A, Wt, qa, sa, qw, sw, out
+    # every row: median as "us" (the rates above), plus mean and min, all
+    # measured after a cache flush
+    timer_of = {"requant_T_128x1_fp8": "requant_fp8", "requant_T_128x1_bf16": "requant_bf16",
+                "encode_e5m6": "e5m6_enc", "decode_e5m6": "e5m6_dec", "gemm_wgrad_row_f32": "wgrad",
+                "transpose_w_128x128": "transpose_w", "gemm_dgrad_bf16": "dgrad"}
+    for tag in ("up", "down"):
+        timer_of.update({f"quant_act_moe_{tag}": f"qa_{tag}", f"quant_w_moe_{tag}": f"qw_{tag}",
+                         f"grouped_gemm_{tag}": f"grouped_{tag}"})
+    for key, tname in timer_of.items():
+        st = stats[tname]
+        rows[key].update({"us_mean": st["us"], "us_median": st["us_median"], "us_min": st["us_min"],
+                          "calls": st["calls"], "timing": f"after a {FLUSH_BYTES >> 30} GiB cache flush per call"})
     return rows
 
 
@@ -365,6 +415,12 @@ def main():
         "gemm_bf16_block": {"shape": f"M{M} N{N} K{K}", "us": ms_g * 1e3, "TFLOP/s": gemm_tflops,
                             "frac_fp8_peak": gemm_tflops / FP8_PEAK_TFLOPS},
     }
+    for key, tname in (("quant_act_1x128", "quant_act"), ("quant_w_128x128", "quant_w"),
+                       ("gemm_bf16_block", "gemm")):
+        st = kt.stats_us(tname)
+        kernels[key].update({"us_median": st["us_median"], "us_min": st["us_min"],
+                             "timing": "inside the step (the other kernels of the step stream "
+                                       "> 500 MB between two calls of one kernel)"})
     result = {
         "metric": "block-scaled FP8 GEMM TFLOP/s (%FP8 peak) at K=7168; quantize GB/s (%HBM)",
         "value": flop / (ms_step * 1e-3) / 1e12,

@@ -35,7 +35,9 @@
 //   distinct banks; the direct loads write that layout by fetching, for LDS
 //   slot (row, chunk p), the global chunk p ^ swizzle(row).  Buffer
 //   descriptors bound each copy to the tile's valid rows (rows past the
-//   end read as zeros), so every per-copy offset is uniform.
+//   end read as zeros): every row offset is in the VGPR offset, which the
+//   range check covers; the SGPR offset carries only the K group's column
+//   offset, which keeps a valid row's address inside that row.
 // * The FP32 scales travel in blocks of 4 K groups through a 3-slot LDS
 //   ring, one quarter block per K group: each lane fetches 4 consecutive
 //   groups of one row, so a row's scales cost one cache line per 4 groups
@@ -453,11 +455,14 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   constexpr int SLOT = C::slot_bytes(BROW);
 
   // this wave's copy u of quarter q of scale block h
-  // (hs = h % NSLOT, passed separately so that it can be a constant)
+  // (hs = h % NSLOT, passed separately so that it can be a constant).  The
+  // quarter's row offset and the block's group offset are added to the
+  // VGPR offset, so the descriptor's range check covers the whole address
+  // (the SGPR offset stays zero).
   auto issue_scales = [&](int u, int q, int h, int hs) {
     const ScaleCopy& x = sc[u];
     const uint32_t dst = lds_base + C::sc_area() + hs * x.slot + x.dst0 + x.dstq * q;
-    gemm_copy4(x.rs, x.voff, x.qstep * q + x.hstep * h, dst);
+    gemm_copy4(x.rs, x.voff + x.qstep * q + x.hstep * h, 0, dst);
   };
   // part k of issue t: tile copy k (k < DPW) of K group min(t, G - 1) into
   // `stage`, or (k >= DPW) copy k - DPW of quarter t % 4 of scale block

@@ -112,8 +112,42 @@ def _ptr(t):
 
 def _ld(t):
     """Row stride (elements) of a row-major 2-D tensor view."""
-    assert t.dim() == 2 and t.stride(1) == 1, "rows must be contiguous"
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"expected a 2-D tensor with contiguous rows, got shape {tuple(t.shape)} "
+                         f"strides {tuple(t.stride())}")
     return t.stride(0)
+
+
+_CODES = ("uint8", "float8_e4m3fn")
+
+
+def _check(t, what, shape, dtypes, contiguous=False):
+    """Refuse a tensor whose shape or dtype does not fit what the kernels
+    will read or write (a short output would be written past its end).
+    shape entries: an int (exact), (">=", n) (at least n) or None (any)."""
+    if t is None:
+        raise ValueError(f"{what}: missing tensor")
+    if str(t.dtype).replace("torch.", "") not in dtypes:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected one of {dtypes}")
+    if t.dim() != len(shape):
+        raise ValueError(f"{what}: {t.dim()}-D tensor, expected {len(shape)}-D")
+    for i, want in enumerate(shape):
+        got = t.shape[i]
+        if want is None:
+            continue
+        if isinstance(want, tuple):
+            if got < want[1]:
+                raise ValueError(f"{what}: dimension {i} is {got}, needs at least {want[1]}")
+        elif got != want:
+            raise ValueError(f"{what}: dimension {i} is {got}, expected {want}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    if t.dim() == 2:
+        _ld(t)
+
+
+def _groups(K):
+    return K // 128
 
 
 def _stream(stream):
@@ -138,6 +172,9 @@ def _call(name, *args):
 def fp8bs_quant_act_1x128(x, q, s, stream=None):
     """x bf16 [M][K] -> q u8 [M][K], s f32 [M][K/128]."""
     M, K = x.shape
+    _check(x, "x", (M, K), ("bfloat16",))
+    _check(q, "q", (M, K), _CODES)
+    _check(s, "s", (M, (">=", _groups(K))), ("float32",))
     _call("fp8bs_quant_act_1x128", _ptr(x), M, K, _ld(x), _ptr(q), _ld(q), _ptr(s), _ld(s),
           _stream(stream))
 
@@ -145,32 +182,47 @@ def fp8bs_quant_act_1x128(x, q, s, stream=None):
 def fp8bs_quant_w_128x128(w, q, s, stream=None):
     """w bf16 [N][K] -> q u8 [N][K], s f32 [ceil(N/128)][K/128]."""
     N, K = w.shape
+    _check(w, "w", (N, K), ("bfloat16",))
+    _check(q, "q", (N, K), _CODES)
+    _check(s, "s", ((N + 127) // 128, (">=", _groups(K))), ("float32",))
     _call("fp8bs_quant_w_128x128", _ptr(w), N, K, _ld(w), _ptr(q), _ld(q), _ptr(s), _ld(s),
           _stream(stream))
 
 
 def fp8bs_quant_per_tensor(x, q, s, stream=None):
     """x bf16 (contiguous, n % 128 == 0) -> q u8 (same shape), s f32 [1]."""
-    assert x.is_contiguous() and q.is_contiguous()
+    if not (x.is_contiguous() and q.is_contiguous()) or q.numel() != x.numel():
+        raise ValueError("x and q must be contiguous with the same number of elements")
+    if str(x.dtype) != "torch.bfloat16" or str(q.dtype).replace("torch.", "") not in _CODES:
+        raise ValueError("x must be bfloat16 and q uint8 codes")
+    if s is None or s.numel() < 1 or str(s.dtype) != "torch.float32":
+        raise ValueError("s must hold one float32")
     _call("fp8bs_quant_per_tensor", _ptr(x), x.numel(), _ptr(q), _ptr(s), _stream(stream))
 
 
 def fp8bs_cast_e4m3(x, q, stream=None):
     """x f32 (contiguous) -> q u8 (same number of elements): nearest-even
     E4M3 codes, saturated to +-448."""
-    assert x.is_contiguous() and q.is_contiguous() and q.numel() == x.numel()
+    if not (x.is_contiguous() and q.is_contiguous()) or q.numel() != x.numel():
+        raise ValueError("x and q must be contiguous with the same number of elements")
+    if str(x.dtype) != "torch.float32" or str(q.dtype).replace("torch.", "") not in _CODES:
+        raise ValueError("x must be float32 and q uint8 codes")
     _call("fp8bs_cast_e4m3", _ptr(x), x.numel(), _ptr(q), _stream(stream))
 
 
 def fp8bs_encode_e5m6(x, y, stream=None):
     """bf16 x [T][C] -> packed E5M6 y u8 [T][>= 1.5 C]."""
     T, C = x.shape
+    _check(x, "x", (T, C), ("bfloat16",))
+    _check(y, "y", (T, (">=", (3 * C + 1) // 2)), ("uint8",))
     _call("fp8bs_encode_e5m6", _ptr(x), T, C, _ld(x), _ptr(y), _ld(y), _stream(stream))
 
 
 def fp8bs_decode_e5m6(y, x, stream=None):
     """packed E5M6 y u8 [T][>= 1.5 C] -> bf16 x [T][C] (exact)."""
     T, C = x.shape
+    _check(x, "x", (T, C), ("bfloat16",))
+    _check(y, "y", (T, (">=", (3 * C + 1) // 2)), ("uint8",))
     _call("fp8bs_decode_e5m6", _ptr(y), T, C, _ld(y), _ptr(x), _ld(x), _stream(stream))
 
 
@@ -178,6 +230,13 @@ def fp8bs_requant_T_128x1(src, x, s_in, q_out, s_out, stream=None):
     """x [T][C] (codes with s_in [T][C/128], or bf16) -> q_out [C][T],
     s_out [C][ceil(T/128)]."""
     T, C = x.shape
+    if int(src) == SRC_FP8_1x128:
+        _check(x, "x", (T, C), _CODES)
+        _check(s_in, "s_in", (T, (">=", _groups(C))), ("float32",))
+    else:
+        _check(x, "x", (T, C), ("bfloat16",))
+    _check(q_out, "q_out", (C, T), _CODES)
+    _check(s_out, "s_out", (C, (">=", (T + 127) // 128)), ("float32",))
     lds_in = _ld(s_in) if s_in is not None else 0
     _call("fp8bs_requant_T_128x1", int(src), _ptr(x), _ptr(s_in), T, C, _ld(x), lds_in,
           _ptr(q_out), _ld(q_out), _ptr(s_out), _ld(s_out), _stream(stream))
@@ -187,14 +246,30 @@ def fp8bs_transpose_w_128x128(q, s, qt, st, stream=None):
     """Codes q [N][K] with 128x128 block scales s [N/128][K/128] -> their
     transpose qt [K][N], st [K/128][N/128]."""
     N, K = q.shape
+    _check(q, "q", (N, K), _CODES)
+    _check(s, "s", ((N + 127) // 128, (">=", _groups(K))), ("float32",))
+    _check(qt, "qt", (K, N), _CODES)
+    _check(st, "st", (_groups(K), (">=", (N + 127) // 128)), ("float32",))
     _call("fp8bs_transpose_w_128x128", _ptr(q), N, K, _ld(q), _ptr(s), _ld(s), _ptr(qt), _ld(qt),
           _ptr(st), _ld(st), _stream(stream))
+
+
+def _check_gemm_operands(a, sa, b, sb, bmode):
+    M, K = a.shape
+    N = b.shape[0]
+    _check(a, "a", (M, K), _CODES)
+    _check(sa, "sa", (M, (">=", _groups(K))), ("float32",))
+    _check(b, "b", (N, K), _CODES)
+    rows_sb = N if int(bmode) == BSCALE_ROW_1x128 else (N + 127) // 128
+    _check(sb, "sb", (rows_sb, (">=", _groups(K))), ("float32",))
 
 
 def fp8bs_gemm(a, sa, b, sb, bmode, d, dt, stream=None):
     """D [M][N] = A [M][K] * B [N][K]^T with block scales."""
     M, K = a.shape
     N = b.shape[0]
+    _check_gemm_operands(a, sa, b, sb, bmode)
+    _check(d, "d", (M, N), ("float32",) if int(dt) == OUT_F32 else ("bfloat16",))
     _call("fp8bs_gemm", _ptr(a), _ptr(sa), _ld(a), _ld(sa), _ptr(b), _ptr(sb), _ld(b), _ld(sb),
           int(bmode), _ptr(d), _ld(d), int(dt), M, N, K, _stream(stream))
 
@@ -204,6 +279,9 @@ def fp8bs_gemm_quant_1x128(a, sa, b, sb, bmode, q, s, stream=None):
     q u8 [M][N], s f32 [M][N/128]."""
     M, K = a.shape
     N = b.shape[0]
+    _check_gemm_operands(a, sa, b, sb, bmode)
+    _check(q, "q", (M, N), _CODES)
+    _check(s, "s", (M, (">=", N // 128)), ("float32",))
     _call("fp8bs_gemm_quant_1x128", _ptr(a), _ptr(sa), _ld(a), _ld(sa), _ptr(b), _ptr(sb), _ld(b),
           _ld(sb), int(bmode), _ptr(q), _ld(q), _ptr(s), _ld(s), M, N, K, _stream(stream))
 
@@ -212,6 +290,12 @@ def fp8bs_grouped_gemm(a, sa, b, sb, offsets, d, dt, stream=None):
     """Per-expert D rows = A rows * B[e]^T; offsets int32 [E+1] on the device."""
     M_total, K = a.shape
     E, N, _ = b.shape
+    _check(a, "a", (M_total, K), _CODES, contiguous=True)
+    _check(sa, "sa", (M_total, (">=", _groups(K))), ("float32",))
+    _check(b, "b", (E, N, K), _CODES, contiguous=True)
+    _check(sb, "sb", (E, (N + 127) // 128, _groups(K)), ("float32",), contiguous=True)
+    _check(offsets, "offsets", (E + 1,), ("int32",), contiguous=True)
+    _check(d, "d", (M_total, N), ("float32",) if int(dt) == OUT_F32 else ("bfloat16",), contiguous=True)
     _call("fp8bs_grouped_gemm", _ptr(a), _ptr(sa), _ld(sa), _ptr(b), _ptr(sb), _ptr(offsets),
           int(E), M_total, _ptr(d), int(dt), N, K, _stream(stream))
 

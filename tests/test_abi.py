@@ -213,18 +213,78 @@ def test_valid_call_without_gpu_reports_no_device():
 
 
 def test_python_binding_raises_on_error():
+    import torch
+
     class Fake:
         shape = (4, 100)
         is_cuda = True
+        def __init__(self, dtype):
+            self.dtype = dtype
         def data_ptr(self):
             return A
         def stride(self, i):
             return (100, 1)[i]
         def dim(self):
             return 2
+        def is_contiguous(self):
+            return True
     with pytest.raises(fp8bs.Fp8bsError) as ei:
-        fp8bs.fp8bs_quant_act_1x128(Fake(), Fake(), Fake(), stream=0)
+        fp8bs.fp8bs_quant_act_1x128(Fake(torch.bfloat16), Fake(torch.uint8), Fake(torch.float32), stream=0)
     assert ei.value.status == fp8bs.ERR_UNSUPPORTED_SHAPE
+
+
+def test_binding_refuses_mismatched_outputs():
+    """Shapes, dtypes and contiguity are checked before any pointer is
+    passed: a short output would otherwise be written past its end."""
+    import torch
+    x = torch.zeros((256, 256), dtype=torch.bfloat16)
+    q = torch.zeros((256, 256), dtype=torch.uint8)
+    s = torch.zeros((256, 2), dtype=torch.float32)
+    with pytest.raises(ValueError, match="dimension 0"):
+        fp8bs.fp8bs_quant_act_1x128(x, q[:200], s, stream=0)
+    with pytest.raises(ValueError, match="dimension 1"):
+        fp8bs.fp8bs_quant_act_1x128(x, q, s[:, :1], stream=0)
+    with pytest.raises(ValueError, match="dtype"):
+        fp8bs.fp8bs_quant_act_1x128(x.float(), q, s, stream=0)
+    with pytest.raises(ValueError, match="dimension 0"):
+        fp8bs.fp8bs_quant_w_128x128(x, q, s[:1], stream=0)
+    a = torch.zeros((300, 256), dtype=torch.uint8)
+    sa = torch.zeros((300, 2), dtype=torch.float32)
+    b = torch.zeros((384, 256), dtype=torch.uint8)
+    sb = torch.zeros((3, 2), dtype=torch.float32)
+    d = torch.zeros((300, 384), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="dimension 0"):
+        fp8bs.fp8bs_gemm(a, sa, b, sb, fp8bs.BSCALE_BLOCK_128x128, d[:299], fp8bs.OUT_BF16, stream=0)
+    with pytest.raises(ValueError, match="dtype"):
+        fp8bs.fp8bs_gemm(a, sa, b, sb, fp8bs.BSCALE_BLOCK_128x128, d, fp8bs.OUT_F32, stream=0)
+    with pytest.raises(ValueError, match="dimension 0"):   # row mode needs a scale row per B row
+        fp8bs.fp8bs_gemm(a, sa, b, sb, fp8bs.BSCALE_ROW_1x128, d, fp8bs.OUT_BF16, stream=0)
+    with pytest.raises(ValueError, match="dimension 0"):
+        fp8bs.fp8bs_gemm(a, sa[:100], b, sb, fp8bs.BSCALE_BLOCK_128x128, d, fp8bs.OUT_BF16, stream=0)
+    with pytest.raises(ValueError, match="rows"):
+        fp8bs.fp8bs_gemm(a.t(), sa, b, sb, fp8bs.BSCALE_BLOCK_128x128, d, fp8bs.OUT_BF16, stream=0)
+    qo = torch.zeros((300, 384), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="dimension 1"):
+        fp8bs.fp8bs_gemm_quant_1x128(a, sa, b, sb, fp8bs.BSCALE_BLOCK_128x128, qo,
+                                     torch.zeros((300, 2), dtype=torch.float32), stream=0)
+    # grouped: contiguous operands, offsets of E + 1 int32
+    bg = torch.zeros((2, 384, 256), dtype=torch.uint8)
+    sbg = torch.zeros((2, 3, 2), dtype=torch.float32)
+    off = torch.zeros((3,), dtype=torch.int32)
+    with pytest.raises(ValueError, match="offsets"):
+        fp8bs.fp8bs_grouped_gemm(a, sa, bg, sbg, off[:2], d, fp8bs.OUT_BF16, stream=0)
+    with pytest.raises(ValueError, match="contiguous"):
+        fp8bs.fp8bs_grouped_gemm(a, sa, bg, sbg, off, torch.zeros((384, 300), dtype=torch.bfloat16).t(),
+                                 fp8bs.OUT_BF16, stream=0)
+    with pytest.raises(ValueError, match="contiguous"):
+        fp8bs.fp8bs_grouped_gemm(torch.zeros((300, 512), dtype=torch.uint8)[:, :256], sa, bg, sbg, off, d,
+                                 fp8bs.OUT_BF16, stream=0)
+    # requant: the transposed output must have C rows of T
+    xq = torch.zeros((256, 384), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="q_out"):
+        fp8bs.fp8bs_requant_T_128x1(fp8bs.SRC_FP8_1x128, xq, torch.zeros((256, 3), dtype=torch.float32),
+                                    torch.zeros((256, 384), dtype=torch.uint8),
+                                    torch.zeros((384, 2), dtype=torch.float32), stream=0)
 
 
 def test_binding_refuses_host_tensors():

@@ -25,7 +25,7 @@ import torch
 import oracle
 from fp8_fine_grained_fp8bs_amd import fp8bs, synth
 from tests.gpu_common import (announce, bf16_dev, check_quant_equal, dev, f32_dev, host,
-                              native_loaded, u8_dev)
+                              native_loaded, record, u8_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -92,6 +92,8 @@ def test_fine_grained_vs_per_tensor_accuracy(idx):
         res[label] = _errs(d, exact)
         announce(f"{name}: {label:48s} rel-Frobenius {res[label][0]:.3e}  max|err|/max|ref| "
                  f"{res[label][1]:.3e}  worst row {res[label][2]:.3e}")
+        record("ablation", f"{name}: {label}", rel_fro=res[label][0], max_err_over_max_ref=res[label][1],
+               worst_row_rel=res[label][2])
     f, t = res["fine-grained FP8 (GPU)"], res["per-tensor FP8 (GPU)"]
     # E4M3 keeps its relative precision over 2^15 of range, so one scale
     # costs accuracy only where the spread of magnitudes pushes ordinary

@@ -19,7 +19,7 @@ import torch
 
 import oracle
 from fp8_fine_grained_fp8bs_amd import fp8bs, synth
-from tests.gpu_common import announce, f32_dev, host, native_loaded, u8_dev
+from tests.gpu_common import announce, f32_dev, host, native_loaded, record, u8_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -76,6 +76,7 @@ def test_accuracy_probe_k4096():
     for title, t in (("accumulation error", acc_table), ("error vs unquantized GEMM", total_table)):
         for k, v in t.items():
             announce(f"{title}: {k:54s} " + "  ".join(f"{m} {x:.3e}" for m, x in v.items()))
+            record("probe_k4096", f"{title}: {k}", **v)
     pa = acc_table["fine-grained FP8, FP32 promotion every 128 K (GPU)"]
     ua = acc_table["per-tensor FP8, unpromoted ~14-bit accumulation model"]
     pt = total_table["fine-grained FP8, promoted (GPU)"]

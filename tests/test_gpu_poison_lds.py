@@ -61,7 +61,7 @@ def test_gemm_quant_poisoned():
 
 
 def test_grouped_poisoned():
-    from tests.gpu_common import check_bf16_is_rounded_f32, check_f32_gemm
+    from tests.gpu_common import check_gemm_outputs
     from tests.test_gpu_gemm import _grouped_dev
     native_loaded()
     counts = np.array([130, 0, 1, 127, 128, 0, 300])
@@ -76,8 +76,7 @@ def test_grouped_poisoned():
     ref = oracle.grouped_gemm(qa, sa, qb, sb, off)
     mag = oracle.grouped_gemm(qa & 0x7F, np.abs(sa), qb & 0x7F, np.abs(sb), off)
     d32 = host(_grouped_dev(qa, sa, qb, sb, off, True))
-    check_f32_gemm("poisoned grouped f32", d32, ref, mag)
-    check_bf16_is_rounded_f32("poisoned grouped bf16", host(_grouped_dev(qa, sa, qb, sb, off, False)), d32)
+    check_gemm_outputs("poisoned grouped", d32, host(_grouped_dev(qa, sa, qb, sb, off, False)), ref, mag)
 
 
 @pytest.mark.parametrize("T", [1, 1000, 8200])
