@@ -2,8 +2,9 @@
 """Benchmark of the fine-grained FP8 hot path on one MI355X (gfx950).
 
 One step = one forward pass of the K = 7168 dense MLP up-projection:
-  quantize X [4096][7168] in 1x128 tiles, quantize W [18432][7168] in
-  128x128 blocks, and the block-scaled FP8 GEMM Y = X W^T with BF16 output.
+  quantize X [4096][7168] in 1x128 tiles and W [18432][7168] in 128x128
+  blocks (one launch, fp8bs_quant_act_w), and the block-scaled FP8 GEMM
+  Y = X W^T with BF16 output.
 The inputs (seeded synthetic bf16, the heavy-tailed recipe of
 ``fp8_fine_grained_fp8bs_amd.synth.mlp_up``) are resident in HBM before the
 timed region starts.  ``value`` is the step's throughput in GEMM TFLOP/s
@@ -176,6 +177,42 @@ def cpu_baseline(x_u16, w_u16, M, N, K):
                        f"({t_qw:.2f} s), GEMM of {g_rows}/{M} rows x {N} x {K} ({t_g:.2f} s); "
                        f"extrapolated to the full step = {est:.1f} s"),
             "seconds_measured": t_qa + t_qw + t_g}
+
+
+def time_quant_split(dev, X, W, qx, sx, qw, sw, reps=20, warm=3):
+    """The step's quantization as two launches (quant_act, then quant_w)
+    and as one (quant_act_w), each call after a cache flush."""
+    import torch
+    from fp8_fine_grained_fp8bs_amd import fp8bs
+    M, K = X.shape
+    N = W.shape[0]
+    b_qa = M * K * 3 + M * (K // 128) * 4
+    b_qw = N * K * 3 + (N // 128) * (K // 128) * 4
+    flush = CacheFlush(dev)
+    log("rows: step quantization, one and two launches")
+    fns = {"qa": lambda: fp8bs.fp8bs_quant_act_1x128(X, qx, sx),
+           "qw": lambda: fp8bs.fp8bs_quant_w_128x128(W, qw, sw),
+           "qaw": lambda: fp8bs.fp8bs_quant_act_w(X, qx, sx, W, qw, sw)}
+    for fn in fns.values():
+        for _ in range(warm):
+            fn()
+    torch.cuda._sleep(QUEUE_FILL_CYCLES)
+    kt = KernelTimer()
+    for _ in range(reps):
+        for name, fn in fns.items():
+            flush()
+            kt.run(name, fn)
+    torch.cuda.synchronize()
+    out = {}
+    for key, name, b, shape in (("quant_act_1x128", "qa", b_qa, f"[{M}][{K}]"),
+                                ("quant_w_128x128", "qw", b_qw, f"[{N}][{K}]"),
+                                ("quant_act_w", "qaw", b_qa + b_qw, f"X [{M}][{K}] + W [{N}][{K}]")):
+        st = kt.stats_us(name)
+        us = st["us_median"]
+        out[key] = {"shape": shape, "us": us, "GB/s": b / us / 1e3, "frac_hbm": b / us / 1e3 / HBM_PEAK_GBS,
+                    "bytes": b, "us_mean": st["us"], "us_median": us, "us_min": st["us_min"], "calls": st["calls"],
+                    "timing": f"after a {FLUSH_BYTES >> 30} GiB cache flush per call"}
+    return out
 
 
 def time_fused(dev, qx, sx, qw, sw, Y, reps=20, warm=3):
@@ -382,8 +419,7 @@ def main():
     kt = KernelTimer()
 
     def step():
-        kt.run("quant_act", lambda: fp8bs.fp8bs_quant_act_1x128(X, qx, sx))
-        kt.run("quant_w", lambda: fp8bs.fp8bs_quant_w_128x128(W, qw, sw))
+        kt.run("quant_act_w", lambda: fp8bs.fp8bs_quant_act_w(X, qx, sx, W, qw, sw))
         kt.run("gemm", lambda: fp8bs.fp8bs_gemm(qx, sx, qw, sw, fp8bs.BSCALE_BLOCK_128x128, Y, fp8bs.OUT_BF16))
 
     log(f"warmup {args.warmup} steps")
@@ -401,22 +437,20 @@ def main():
     ms_step = wall / args.steps * 1e3
     assert torch.isfinite(Y.float()).all(), "non-finite GEMM output"
 
-    ms_qa, ms_qw, ms_g = kt.mean_ms("quant_act"), kt.mean_ms("quant_w"), kt.mean_ms("gemm")
+    ms_q, ms_g = kt.mean_ms("quant_act_w"), kt.mean_ms("gemm")
     flop = 2.0 * M * N * K
     b_qa = M * K * 3 + M * (K // 128) * 4
     b_qw = N * K * 3 + (N // 128) * (K // 128) * 4
+    b_q = b_qa + b_qw
     gemm_tflops = flop / ms_g / 1e9
     traffic = read_traffic()
     kernels = {
-        "quant_act_1x128": {"shape": f"[{M}][{K}]", "us": ms_qa * 1e3, "GB/s": b_qa / ms_qa / 1e6,
-                            "frac_hbm": b_qa / ms_qa / 1e6 / HBM_PEAK_GBS, "bytes": b_qa},
-        "quant_w_128x128": {"shape": f"[{N}][{K}]", "us": ms_qw * 1e3, "GB/s": b_qw / ms_qw / 1e6,
-                            "frac_hbm": b_qw / ms_qw / 1e6 / HBM_PEAK_GBS, "bytes": b_qw},
+        "quant_act_w": {"shape": f"X [{M}][{K}] 1x128 + W [{N}][{K}] 128x128, one launch", "us": ms_q * 1e3,
+                        "GB/s": b_q / ms_q / 1e6, "frac_hbm": b_q / ms_q / 1e6 / HBM_PEAK_GBS, "bytes": b_q},
         "gemm_bf16_block": {"shape": f"M{M} N{N} K{K}", "us": ms_g * 1e3, "TFLOP/s": gemm_tflops,
                             "frac_fp8_peak": gemm_tflops / FP8_PEAK_TFLOPS},
     }
-    for key, tname in (("quant_act_1x128", "quant_act"), ("quant_w_128x128", "quant_w"),
-                       ("gemm_bf16_block", "gemm")):
+    for key, tname in (("quant_act_w", "quant_act_w"), ("gemm_bf16_block", "gemm")):
         st = kt.stats_us(tname)
         kernels[key].update({"us_median": st["us_median"], "us_min": st["us_min"],
                              "timing": "inside the step (the other kernels of the step stream "
@@ -434,8 +468,9 @@ def main():
         "vs_baseline": None,
         "dtype": "e4m3 (fp32 accumulate, bf16 out)",
         "data": "synthetic",
-        "config": {"workload": "dense MLP up-projection forward: quant_act 1x128 of X[4096][7168] + "
-                               "quant_w 128x128 of W[18432][7168] + block-scaled FP8 GEMM Y=X*W^T (BF16 out)",
+        "config": {"workload": "dense MLP up-projection forward: 1x128 quantization of X[4096][7168] and "
+                               "128x128 quantization of W[18432][7168] (one launch) + block-scaled FP8 GEMM "
+                               "Y=X*W^T (BF16 out)",
                    "M": M, "N": N, "K": K, "inputs": "bf16 X ~N(0,1) with 1% Student-t(3) channels, "
                                                     "W ~N(0,0.006), seed 0"},
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": FP8_PEAK_TFLOPS,
@@ -444,7 +479,8 @@ def main():
         "kernels": kernels,
     }
     if args.rows == "all":
-        rows = time_fused(dev, qx, sx, qw, sw, Y)
+        rows = time_quant_split(dev, X, W, qx, sx, qw, sw)
+        rows.update(time_fused(dev, qx, sx, qw, sw, Y))
         rows.update(time_rows(dev))
         result["rows"] = rows
     if args.cpu_baseline == "on":

@@ -106,6 +106,29 @@ fp8bs_status fp8bs_quant_act_1x128(const void* x, int64_t M, int64_t K, int64_t 
                                                 s, lds, static_cast<hipStream_t>(stream)));
 }
 
+fp8bs_status fp8bs_quant_act_w(const void* x, int64_t M, int64_t ldx, uint8_t* qx, int64_t ldqx,
+                               float* sx, int64_t ldsx, const void* w, int64_t N, int64_t ldw,
+                               uint8_t* qw, int64_t ldqw, float* sw, int64_t ldsw, int64_t K,
+                               void* stream) {
+  if (M < 0 || N < 0 || K <= 0) return FP8BS_ERR_INVALID_ARG;
+  if (K % 128 != 0) return FP8BS_ERR_UNSUPPORTED_SHAPE;
+  if (M == 0 && N == 0) return FP8BS_OK;
+  if (M > 0) {
+    FP8BS_TRY(check_matrix(x, K, ldx, 2));
+    FP8BS_TRY(check_matrix(qx, K, ldqx, 1));
+    FP8BS_TRY(check_scales(sx, K / 128, ldsx));
+  }
+  if (N > 0) {
+    FP8BS_TRY(check_matrix(w, K, ldw, 2));
+    FP8BS_TRY(check_matrix(qw, K, ldqw, 1));
+    FP8BS_TRY(check_scales(sw, K / 128, ldsw));
+  }
+  FP8BS_TRY(check_device());
+  return launched(fp8bs::launch_quant_act_w(static_cast<const uint16_t*>(x), M, ldx, qx, ldqx, sx, ldsx,
+                                            static_cast<const uint16_t*>(w), N, ldw, qw, ldqw, sw, ldsw,
+                                            K, static_cast<hipStream_t>(stream)));
+}
+
 fp8bs_status fp8bs_quant_w_128x128(const void* w, int64_t N, int64_t K, int64_t ldw,
                                    uint8_t* q, int64_t ldq, float* s, int64_t lds,
                                    void* stream) {

@@ -99,13 +99,13 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
 // One wave per row, all of the row's tile-quads loaded before any is
 // encoded (up to U KiB in flight per wave): the better shape once the
 // matrix is large enough to keep every compute unit busy for several rows.
+// `blk` is the workgroup's index among the row workgroups (4 rows each).
 template <int U>
-__global__ __launch_bounds__(256) void quant_act_row_kernel(const uint16_t* __restrict__ x, int64_t M,
-                                                        int G, int64_t ldx, uint8_t* __restrict__ q,
-                                                        int64_t ldq, float* __restrict__ s,
-                                                        int64_t lds) {
+__device__ __forceinline__ void act_rows(const uint16_t* __restrict__ x, int64_t M, int G, int64_t ldx,
+                                         uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s,
+                                         int64_t lds, int64_t blk) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t row = blk * 4 + (threadIdx.x >> 6);
   if (row >= M) return;  // uniform per wave
   const int sub = lane & 15;
   const int grp = lane >> 4;
@@ -146,6 +146,14 @@ __global__ __launch_bounds__(256) void quant_act_row_kernel(const uint16_t* __re
   }
 }
 
+template <int U>
+__global__ __launch_bounds__(256) void quant_act_row_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                        int G, int64_t ldx, uint8_t* __restrict__ q,
+                                                        int64_t ldq, float* __restrict__ s,
+                                                        int64_t lds) {
+  act_rows<U>(x, M, G, ldx, q, ldq, s, lds, blockIdx.x);
+}
+
 // ---------------------------------------------------------------------
 // 128x128 weight blocks.  One 256-thread workgroup per block: thread t
 // holds rows (t>>4) + 16 i, i < 8, and the 8 bf16 at column 8 (t & 15) of
@@ -153,14 +161,9 @@ __global__ __launch_bounds__(256) void quant_act_row_kernel(const uint16_t* __re
 // pass and the encode pass (one HBM read).  Rows past N are skipped and
 // do not enter the max-abs.
 // ---------------------------------------------------------------------
-__global__ __launch_bounds__(256) void quant_w_kernel(const uint16_t* __restrict__ w, int64_t N,
-                                                      int64_t ldw, uint8_t* __restrict__ q,
-                                                      int64_t ldq, float* __restrict__ s,
-                                                      int64_t lds) {
-  __shared__ float wave_amax[4];
-  poison_lds<sizeof(wave_amax)>(wave_amax);
-  const int g = blockIdx.x;
-  const int64_t nb = blockIdx.y;
+__device__ __forceinline__ void w_block(const uint16_t* __restrict__ w, int64_t N, int64_t ldw,
+                                        uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s,
+                                        int64_t lds, int g, int64_t nb, float* wave_amax) {
   const int tid = threadIdx.x;
   const int col = (tid & 15) * 8;
   const int r0 = tid >> 4;
@@ -200,6 +203,42 @@ __global__ __launch_bounds__(256) void quant_w_kernel(const uint16_t* __restrict
     c.x = encode4(f, t);
     c.y = encode4(f + 4, t);
     if (n < N) *reinterpret_cast<uint2*>(q + n * ldq + static_cast<int64_t>(g) * 128 + col) = c;
+  }
+}
+
+__global__ __launch_bounds__(256) void quant_w_kernel(const uint16_t* __restrict__ w, int64_t N,
+                                                      int64_t ldw, uint8_t* __restrict__ q,
+                                                      int64_t ldq, float* __restrict__ s,
+                                                      int64_t lds) {
+  __shared__ float wave_amax[4];
+  poison_lds<sizeof(wave_amax)>(wave_amax);
+  w_block(w, N, ldw, q, ldq, s, lds, blockIdx.x, blockIdx.y, wave_amax);
+}
+
+// ---------------------------------------------------------------------
+// A layer's activation (1x128 tiles) and weight (128x128 blocks) in one
+// launch: the first act_blocks workgroups take 4 activation rows each,
+// the others one weight block each (block row (b - act_blocks) / G,
+// K group (b - act_blocks) % G).  Both streams share one ramp-up and drain
+// instead of two back-to-back launches, and the smaller activation
+// matrix runs beside the weight blocks.
+// ---------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(256) void quant_act_w_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                          int64_t ldx, uint8_t* __restrict__ qx,
+                                                          int64_t ldqx, float* __restrict__ sx,
+                                                          int64_t ldsx, const uint16_t* __restrict__ w,
+                                                          int64_t N, int64_t ldw, uint8_t* __restrict__ qw,
+                                                          int64_t ldqw, float* __restrict__ sw,
+                                                          int64_t ldsw, int G, int64_t act_blocks) {
+  __shared__ float wave_amax[4];
+  poison_lds<sizeof(wave_amax)>(wave_amax);
+  const int64_t b = blockIdx.x;
+  if (b < act_blocks) {
+    act_rows<U>(x, M, G, ldx, qx, ldqx, sx, ldsx, b);
+  } else {
+    const int64_t wb = b - act_blocks;
+    w_block(w, N, ldw, qw, ldqw, sw, ldsw, static_cast<int>(wb % G), wb / G, wave_amax);
   }
 }
 
@@ -343,6 +382,33 @@ hipError_t launch_quant_act_1x128(const uint16_t* x, int64_t M, int64_t K, int64
   if (quads <= 8) return launch_act_rows<8>(x, M, G, ldx, q, ldq, s, lds, st);
   if (quads <= 14) return launch_act_rows<14>(x, M, G, ldx, q, ldq, s, lds, st);
   return launch_act_rows<16>(x, M, G, ldx, q, ldq, s, lds, st);
+}
+
+template <int U>
+hipError_t launch_act_w_u(const uint16_t* x, int64_t M, int64_t ldx, uint8_t* qx, int64_t ldqx, float* sx,
+                          int64_t ldsx, const uint16_t* w, int64_t N, int64_t ldw, uint8_t* qw,
+                          int64_t ldqw, float* sw, int64_t ldsw, int G, hipStream_t st) {
+  const int64_t act_blocks = (M + 3) / 4;
+  const int64_t blocks = act_blocks + ((N + 127) / 128) * G;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_act_w_kernel<U>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, x, M,
+                     ldx, qx, ldqx, sx, ldsx, w, N, ldw, qw, ldqw, sw, ldsw, G, act_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act_w(const uint16_t* x, int64_t M, int64_t ldx, uint8_t* qx, int64_t ldqx,
+                              float* sx, int64_t ldsx, const uint16_t* w, int64_t N, int64_t ldw,
+                              uint8_t* qw, int64_t ldqw, float* sw, int64_t ldsw, int64_t K,
+                              hipStream_t st) {
+  if (K / 128 > (1 << 30)) return hipErrorInvalidValue;
+  const int G = static_cast<int>(K / 128);
+  const int quads = (G + 3) / 4;
+  if (quads <= 1) return launch_act_w_u<1>(x, M, ldx, qx, ldqx, sx, ldsx, w, N, ldw, qw, ldqw, sw, ldsw, G, st);
+  if (quads <= 2) return launch_act_w_u<2>(x, M, ldx, qx, ldqx, sx, ldsx, w, N, ldw, qw, ldqw, sw, ldsw, G, st);
+  if (quads <= 4) return launch_act_w_u<4>(x, M, ldx, qx, ldqx, sx, ldsx, w, N, ldw, qw, ldqw, sw, ldsw, G, st);
+  if (quads <= 8) return launch_act_w_u<8>(x, M, ldx, qx, ldqx, sx, ldsx, w, N, ldw, qw, ldqw, sw, ldsw, G, st);
+  if (quads <= 14) return launch_act_w_u<14>(x, M, ldx, qx, ldqx, sx, ldsx, w, N, ldw, qw, ldqw, sw, ldsw, G, st);
+  return launch_act_w_u<16>(x, M, ldx, qx, ldqx, sx, ldsx, w, N, ldw, qw, ldqw, sw, ldsw, G, st);
 }
 
 hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,

@@ -31,7 +31,8 @@ BSCALE_ROW_1x128 = 1
 SRC_FP8_1x128 = 0
 SRC_BF16 = 1
 
-ENTRY_POINTS = ("fp8bs_quant_act_1x128", "fp8bs_quant_w_128x128", "fp8bs_quant_per_tensor",
+ENTRY_POINTS = ("fp8bs_quant_act_1x128", "fp8bs_quant_w_128x128", "fp8bs_quant_act_w",
+                "fp8bs_quant_per_tensor",
                 "fp8bs_cast_e4m3",
                 "fp8bs_encode_e5m6", "fp8bs_decode_e5m6", "fp8bs_requant_T_128x1",
                 "fp8bs_transpose_w_128x128", "fp8bs_gemm", "fp8bs_gemm_quant_1x128",
@@ -71,6 +72,7 @@ def load() -> ctypes.CDLL:
     sigs = {
         "fp8bs_quant_act_1x128": [P, I64, I64, I64, P, I64, P, I64, P],
         "fp8bs_quant_w_128x128": [P, I64, I64, I64, P, I64, P, I64, P],
+        "fp8bs_quant_act_w": [P, I64, I64, P, I64, P, I64, P, I64, I64, P, I64, P, I64, I64, P],
         "fp8bs_quant_per_tensor": [P, I64, P, P, P],
         "fp8bs_cast_e4m3": [P, I64, P, P],
         "fp8bs_encode_e5m6": [P, I64, I64, I64, P, I64, P],
@@ -320,6 +322,33 @@ def quant_w_128x128(w, stream=None):
     s = torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32, device=w.device)
     fp8bs_quant_w_128x128(w, q, s, stream)
     return q, s
+
+
+def fp8bs_quant_act_w(x, qx, sx, w, qw, sw, stream=None):
+    """x bf16 [M][K] -> qx, sx (1x128 tiles) and w bf16 [N][K] -> qw, sw
+    (128x128 blocks), in one launch."""
+    M, K = x.shape
+    N = w.shape[0]
+    _check(x, "x", (M, K), ("bfloat16",))
+    _check(qx, "qx", (M, K), _CODES)
+    _check(sx, "sx", (M, (">=", _groups(K))), ("float32",))
+    _check(w, "w", (N, K), ("bfloat16",))
+    _check(qw, "qw", (N, K), _CODES)
+    _check(sw, "sw", ((N + 127) // 128, (">=", _groups(K))), ("float32",))
+    _call("fp8bs_quant_act_w", _ptr(x), M, _ld(x), _ptr(qx), _ld(qx), _ptr(sx), _ld(sx),
+          _ptr(w), N, _ld(w), _ptr(qw), _ld(qw), _ptr(sw), _ld(sw), K, _stream(stream))
+
+
+def quant_act_w(x, w, stream=None):
+    import torch
+    M, K = x.shape
+    N = w.shape[0]
+    qx = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    sx = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    qw = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    sw = torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32, device=w.device)
+    fp8bs_quant_act_w(x, qx, sx, w, qw, sw, stream)
+    return qx, sx, qw, sw
 
 
 def quant_per_tensor(x, stream=None):

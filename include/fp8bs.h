@@ -92,6 +92,24 @@ fp8bs_status fp8bs_quant_w_128x128(const void *w, int64_t N, int64_t K, int64_t 
                                    void *stream);
 
 /*
+ * A layer's activation and weight quantized in one launch: exactly
+ * fp8bs_quant_act_1x128(x, M, K, ...) and fp8bs_quant_w_128x128(w, N, K,
+ * ...) ([p1] para 3: 1x128 activation tiles, 128x128 weight blocks), with
+ * the same codes and scales, run as one kernel so that the two streams
+ * share one ramp-up and drain and the activation runs beside the weight
+ * blocks.
+ *   x  bf16 [M][ldx]   qx u8 [M][ldqx]   sx f32 [M][ldsx]          (K/128 per row)
+ *   w  bf16 [N][ldw]   qw u8 [N][ldqw]   sw f32 [ceil(N/128)][ldsw] (K/128 per row)
+ * M >= 0, N >= 0 (a zero side is skipped, both zero is a no-op), K > 0 and
+ * K % 128 == 0.  Arguments of a non-empty side are checked as in the
+ * single calls; the two sides must not overlap.
+ */
+fp8bs_status fp8bs_quant_act_w(const void *x, int64_t M, int64_t ldx, uint8_t *qx, int64_t ldqx,
+                               float *sx, int64_t ldsx, const void *w, int64_t N, int64_t ldw,
+                               uint8_t *qw, int64_t ldqw, float *sw, int64_t ldsw, int64_t K,
+                               void *stream);
+
+/*
  * Per-tensor scaling: one scale for a whole tensor, the common practice
  * [p3] para 4 describes (the tensor's max-abs mapped to the FP8 maximum)
  * and [p1] para 4 contrasts with the fine-grained tiles.  The comparison

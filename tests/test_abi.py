@@ -42,6 +42,11 @@ def quant_w(w=A, N=4, K=256, ldw=256, q=A, ldq=256, s=A, lds=2):
     return fp8bs.load().fp8bs_quant_w_128x128(w, N, K, ldw, q, ldq, s, lds, NULL)
 
 
+def quant_aw(x=A, M=4, ldx=256, qx=A, ldqx=256, sx=A, ldsx=2, w=A, N=4, ldw=256, qw=A, ldqw=256, sw=A,
+             ldsw=2, K=256):
+    return fp8bs.load().fp8bs_quant_act_w(x, M, ldx, qx, ldqx, sx, ldsx, w, N, ldw, qw, ldqw, sw, ldsw, K, NULL)
+
+
 def quant_pt(x=A, n=256, q=A, s=A):
     return fp8bs.load().fp8bs_quant_per_tensor(x, n, q, s, NULL)
 
@@ -102,6 +107,17 @@ def grouped(a=A, sa=A, ldsa=2, b=A, sb=A, off=A, E=2, M=10, d=A, dt=0, N=128, K=
     (lambda: quant_w(ldq=100), fp8bs.ERR_INVALID_ARG),
     (lambda: quant_w(w=A + 2), fp8bs.ERR_MISALIGNED),
     (lambda: quant_w(N=0), fp8bs.OK),
+    (lambda: quant_aw(K=200, ldx=256, ldqx=256, ldw=256, ldqw=256), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: quant_aw(M=-1), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_aw(N=-1), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_aw(K=0), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_aw(x=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_aw(sw=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_aw(ldqw=128), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_aw(ldsx=1), fp8bs.ERR_INVALID_ARG),
+    (lambda: quant_aw(w=A + 8), fp8bs.ERR_MISALIGNED),
+    (lambda: quant_aw(ldqx=264), fp8bs.ERR_MISALIGNED),
+    (lambda: quant_aw(M=0, N=0, x=NULL, qx=NULL, sx=NULL, w=NULL, qw=NULL, sw=NULL), fp8bs.OK),
     (lambda: quant_pt(n=-128), fp8bs.ERR_INVALID_ARG),
     (lambda: quant_pt(n=200), fp8bs.ERR_UNSUPPORTED_SHAPE),
     (lambda: quant_pt(x=NULL), fp8bs.ERR_INVALID_ARG),

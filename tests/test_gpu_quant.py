@@ -178,3 +178,62 @@ def test_quant_w_ragged_strided_edge_blocks():
         q, s = _run_w(w, ldw_pad=8, ldq_pad=16, lds_pad=1)
         qr, sr = oracle.quant_w_128x128(w)
         check_quant_equal(f"quant_w N={N}", q, s, qr, sr)
+
+
+def _run_act_w(x_u16, w_u16, pad=0):
+    """fp8bs_quant_act_w on host bf16 arrays (rows optionally padded)."""
+    M, K = x_u16.shape
+    N = w_u16.shape[0]
+    G, NB = K // 128, (N + 127) // 128
+    xb = torch.zeros((M, K + pad), dtype=torch.bfloat16, device=dev())
+    wb = torch.zeros((N, K + pad), dtype=torch.bfloat16, device=dev())
+    if M:
+        xb[:, :K] = bf16_dev(x_u16)
+    if N:
+        wb[:, :K] = bf16_dev(w_u16)
+    qx = torch.full((M, K + pad), 0x55, dtype=torch.uint8, device=dev())
+    sx = torch.full((M, G + pad // 16), -1.0, dtype=torch.float32, device=dev())
+    qw = torch.full((N, K + pad), 0x55, dtype=torch.uint8, device=dev())
+    sw = torch.full((NB, G + pad // 16), -1.0, dtype=torch.float32, device=dev())
+    fp8bs.fp8bs_quant_act_w(xb[:, :K], qx[:, :K], sx[:, :G], wb[:, :K], qw[:, :K], sw[:, :G])
+    qxh, sxh, qwh, swh = host(qx), host(sx), host(qw), host(sw)
+    if pad:
+        assert (qxh[:, K:] == 0x55).all() and (qwh[:, K:] == 0x55).all(), "wrote past a code row"
+        assert (sxh[:, G:] == -1.0).all() and (swh[:, G:] == -1.0).all(), "wrote past a scale row"
+    return qxh[:, :K], sxh[:, :G], qwh[:, :K], swh[:, :G]
+
+
+@pytest.mark.parametrize("name", ["tiny", "mlp_up", "moe_down"])
+def test_quant_act_w_one_launch_bit_exact(name):
+    """The layer's activation and weight quantized in one launch: the same
+    codes and scales as the two quantizers (oracle), at full size."""
+    native_loaded()
+    announce(f"quant_act_w {name}")
+    if name == "tiny":
+        d = synth.tiny()
+        x, w = d["A"], d["W"]
+    elif name == "mlp_up":
+        d = synth.mlp_up()
+        x, w = d["X"], d["W"]
+    else:
+        d = synth.moe(parts=("A_down", "W_down"))
+        x, w = d["A_down"], d["W_down"].reshape(-1, 2048)
+    qx, sx, qw, sw = _run_act_w(x, w)
+    check_quant_equal(f"{name} activation", qx, sx, *oracle.quant_act_1x128(x))
+    check_quant_equal(f"{name} weight", qw, sw, *oracle.quant_w_128x128(w))
+
+
+def test_quant_act_w_ragged_strided_and_one_side_empty():
+    native_loaded()
+    rng = np.random.default_rng(77)
+    for M, N, K in ((3, 300, 384), (1000, 1, 128), (0, 200, 512), (130, 0, 1664), (77, 129, 7168)):
+        x = synth.tiny(M=max(M, 1), N=1, K=K, seed=M + K)["A"][:M]
+        w = synth.tiny(M=1, N=max(N, 1), K=K, seed=N + K)["W"][:N]
+        if M >= 3:
+            x = np.concatenate([_edge_rows(K, rng)[:M], x])[:M]
+        announce(f"quant_act_w ragged M={M} N={N} K={K}")
+        qx, sx, qw, sw = _run_act_w(x, w, pad=32)
+        if M:
+            check_quant_equal(f"act M={M} K={K}", qx, sx, *oracle.quant_act_1x128(x))
+        if N:
+            check_quant_equal(f"w N={N} K={K}", qw, sw, *oracle.quant_w_128x128(w))
