@@ -18,6 +18,20 @@
 //   (both exact) with explicit saturation, and a zero scale gives signed
 //   zero codes.
 //
+//   BF16 tiles (every x and amax with at most 8 significant bits) need no
+//   repair step at all (encode4_bf16).  Write v = 448 x / amax, the quotient
+//   by the unrounded scale; x / s = v (amax / 448) / s differs from v by at
+//   most 2^-24 relatively.  Brackets that differ put a midpoint mu within
+//   2^-19.9 of x / s, hence within 2^-19.8 of v.  But 448 x - mu amax is an
+//   integer combination of 7 X 2^(a+6) and N A 2^(b+c) (x = X 2^a,
+//   amax = A 2^b, mu = N 2^c with X, A < 2^8, N < 2^5), so it is zero or at
+//   least 2^-13 of mu amax: differing brackets mean v = mu exactly.  Then
+//   x / s lies below mu when s was rounded up (448 s > amax), above it when
+//   s was rounded down, and on it when s is exact (a tie: the even code);
+//   the sign of 448 s - amax comes exactly from one fma per tile.  In
+//   random BF16 data such brackets differ for about 0.5 % of the values
+//   (amax significands with small odd factors), i.e. in most waves.
+//
 // Scales: s = amax / 448 as an IEEE binary32 division (the library is built
 // without fast-math and keeps FP32 subnormals).
 #pragma once
@@ -74,6 +88,26 @@ __device__ __forceinline__ TileScale make_tile_scale(float amax) {
   return t;
 }
 
+// Per-tile choice for differing brackets of a BF16 tile (see the top of this
+// file): the upper code where the exact quotient lies above the midpoint
+// (the scale was rounded down), the even code on an exact tie (the scale is
+// exact), the lower code otherwise.  As byte masks for resolve_brackets.
+struct Bf16Side {
+  uint32_t up;    // 0x01010101: take the upper code
+  uint32_t even;  // all ones: take the even code
+};
+__device__ __forceinline__ Bf16Side bf16_side(float s, float amax) {
+  const float d = __builtin_fmaf(s, kE4M3Max, -amax);  // 448 s - amax, sign exact
+  return {d < 0.0f ? 0x01010101u : 0u, d == 0.0f ? 0xffffffffu : 0u};
+}
+// Packed codes of two bracketing conversions: where a byte differs the two
+// codes are adjacent magnitudes (same sign, hi = lo + 1, so bit 0 differs);
+// add 1 to lo there when the upper or the even (lo odd) code is chosen.  No
+// carry: lo's magnitude is then at most 0x7D.
+__device__ __forceinline__ uint32_t resolve_brackets(uint32_t lo, uint32_t hi, Bf16Side k) {
+  return lo + ((lo ^ hi) & 0x01010101u & (k.up | (lo & k.even)));
+}
+
 // Decide between two adjacent codes (bracketing magnitudes) for value x and
 // scale s with s >= 2^-100 (or both prescaled by 2^64).
 __device__ __forceinline__ uint32_t resolve_pair(float x, float s, uint32_t c_lo, uint32_t c_hi) {
@@ -126,6 +160,17 @@ __device__ __forceinline__ uint32_t encode4(const float v[4], const TileScale& t
 #pragma unroll
   for (int i = 0; i < 4; ++i) out |= encode_general(v[i], t.s) << (8 * i);
   return out;
+}
+
+// encode4 for a BF16 tile (values and amax with at most 8 significant
+// bits): differing brackets resolve by the tile's side, no repair step.
+__device__ __forceinline__ uint32_t encode4_bf16(const float v[4], const TileScale& t, Bf16Side k) {
+  if (__builtin_expect(t.fast, 1)) {
+    const uint32_t lo = cvt4(v[0] * t.rlo, v[1] * t.rlo, v[2] * t.rlo, v[3] * t.rlo);
+    const uint32_t hi = cvt4(v[0] * t.rhi, v[1] * t.rhi, v[2] * t.rhi, v[3] * t.rhi);
+    return resolve_brackets(lo, hi, k);
+  }
+  return encode4(v, t);
 }
 
 // Max over the 16 lanes of a DPP row (lanes 16r .. 16r+15) of non-negative

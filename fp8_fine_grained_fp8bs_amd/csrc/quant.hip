@@ -64,9 +64,10 @@ __device__ __forceinline__ void act_encode(uint8_t* __restrict__ q, int64_t ldq,
     for (int i = 0; i < 8; ++i) am = __builtin_fmaxf(am, __builtin_fabsf(f[i]));
     am = row16_max(am);
     const TileScale t = make_tile_scale(am);
+    const Bf16Side k = bf16_side(t.s, am);
     uint2 cw;
-    cw.x = encode4(f, t);
-    cw.y = encode4(f + 4, t);
+    cw.x = encode4_bf16(f, t, k);
+    cw.y = encode4_bf16(f + 4, t, k);
     if (g < G) {
       *reinterpret_cast<uint2*>(qr + static_cast<int64_t>(g) * 128) = cw;
       if (sub == 0) sr[g] = t.s;
@@ -135,9 +136,10 @@ __device__ __forceinline__ void act_rows(const uint16_t* __restrict__ x, int64_t
       for (int i = 0; i < 8; ++i) am = __builtin_fmaxf(am, __builtin_fabsf(f[i]));
       am = row16_max(am);
       const TileScale t = make_tile_scale(am);
+      const Bf16Side k = bf16_side(t.s, am);
       uint2 c;
-      c.x = encode4(f, t);
-      c.y = encode4(f + 4, t);
+      c.x = encode4_bf16(f, t, k);
+      c.y = encode4_bf16(f + 4, t, k);
       if (g < G) {
         *reinterpret_cast<uint2*>(qr + g * 128) = c;
         if (sub == 0) sr[g] = t.s;
@@ -193,6 +195,7 @@ __device__ __forceinline__ void w_block(const uint16_t* __restrict__ w, int64_t 
   am = __builtin_fmaxf(__builtin_fmaxf(wave_amax[0], wave_amax[1]),
                        __builtin_fmaxf(wave_amax[2], wave_amax[3]));
   const TileScale t = make_tile_scale(am);
+  const Bf16Side k = bf16_side(t.s, am);
   if (tid == 0) s[nb * lds + g] = t.s;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -200,8 +203,8 @@ __device__ __forceinline__ void w_block(const uint16_t* __restrict__ w, int64_t 
     const float f[8] = {bf16_lo(v[i].x), bf16_hi(v[i].x), bf16_lo(v[i].y), bf16_hi(v[i].y),
                         bf16_lo(v[i].z), bf16_hi(v[i].z), bf16_lo(v[i].w), bf16_hi(v[i].w)};
     uint2 c;
-    c.x = encode4(f, t);
-    c.y = encode4(f + 4, t);
+    c.x = encode4_bf16(f, t, k);
+    c.y = encode4_bf16(f + 4, t, k);
     if (n < N) *reinterpret_cast<uint2*>(q + n * ldq + static_cast<int64_t>(g) * 128 + col) = c;
   }
 }
@@ -301,13 +304,15 @@ __global__ __launch_bounds__(256) void per_tensor_quant_kernel(const uint16_t* _
                                                                int64_t chunks,
                                                                const uint32_t* __restrict__ s_bits,
                                                                uint8_t* __restrict__ q) {
-  const TileScale t = make_tile_scale(__uint_as_float(*s_bits));
+  const float am = __uint_as_float(*s_bits);
+  const TileScale t = make_tile_scale(am);
+  const Bf16Side k = bf16_side(t.s, am);
   for (int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; c < chunks;
        c += static_cast<int64_t>(gridDim.x) * 256) {
     const uint4 v = load16_nt(x + c * 8);
     const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                         bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-    *reinterpret_cast<uint2*>(q + c * 8) = make_uint2(encode4(f, t), encode4(f + 4, t));
+    *reinterpret_cast<uint2*>(q + c * 8) = make_uint2(encode4_bf16(f, t, k), encode4_bf16(f + 4, t, k));
   }
 }
 

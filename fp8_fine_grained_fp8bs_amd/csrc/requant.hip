@@ -130,9 +130,11 @@ __global__ __launch_bounds__(256) void requant_kernel(const uint8_t* __restrict_
       x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xf, 0xf, false));   // lane ^ 2
       x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xf, 0xf, false));  // half-row mirror
       const TileScale ts = make_tile_scale(__int_as_float(x));
+      const Bf16Side side = bf16_side(ts.s, __int_as_float(x));
       uint32_t codes[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) codes[k] = encode4(&v[c][4 * k], ts);
+      for (int k = 0; k < 4; ++k)
+        codes[k] = SRC_BF16 ? encode4_bf16(&v[c][4 * k], ts, side) : encode4(&v[c][4 * k], ts);
       const int64_t ch = c0 + CPT * cg + c;
       uint8_t* dst = q_out + ch * ld_out + tok;
       if (full) {
