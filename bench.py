@@ -373,6 +373,41 @@ def time_rows(dev, reps=20, warm=3):
         rows[f"grouped_gemm_{tag}"] = {"shape": f"E{E} sumM{Ttok} N{N} K{K}", "us": ms * 1e3,
                                        "TFLOP/s": fl / ms / 1e9, "frac_fp8_peak": fl / ms / 1e9 / FP8_PEAK_TFLOPS}
         del A, Wt, qa, sa, qw, sw, out
+    # BF16 A quantized inside the GEMM (the FP8 activation never crosses HBM)
+    # against quant_act + gemm, on the low-rank projections 7168 -> 576 and
+    # 7168 -> 1536 of 4096 tokens (small N: A is re-quantized per 256-column
+    # tile of B, 3 and 6 times)
+    log("rows: bf16-A projections")
+    M, K = 4096, 7168
+    rng = np.random.default_rng(5)
+    Xp = bf16_dev(synth.mlp_up(T=M, K=K, N=1536, seed=1, with_w=False)["X"], dev)
+    qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    for N in (576, 1536):
+        Wp = bf16_dev(synth.bf16_bits((rng.standard_normal((N, K)) * 0.006).astype(np.float32)), dev)
+        qw, sw = fp8bs.quant_w_128x128(Wp)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        fl = 2.0 * M * N * K
+        t_q = timed(f"proj{N}_qa", lambda: fp8bs.fp8bs_quant_act_1x128(Xp, qa, sa))
+        t_g = timed(f"proj{N}_gemm", lambda: fp8bs.fp8bs_gemm(qa, sa, qw, sw, fp8bs.BSCALE_BLOCK_128x128, out,
+                                                               fp8bs.OUT_BF16))
+
+        def pair():
+            fp8bs.fp8bs_quant_act_1x128(Xp, qa, sa)
+            fp8bs.fp8bs_gemm(qa, sa, qw, sw, fp8bs.BSCALE_BLOCK_128x128, out, fp8bs.OUT_BF16)
+        t_p = timed(f"proj{N}_pair", pair)
+        t_a = timed(f"proj{N}_bf16a", lambda: fp8bs.fp8bs_gemm_bf16a(Xp, None, None, qw, sw, out, fp8bs.OUT_BF16))
+        t_c = timed(f"proj{N}_bf16a_codes", lambda: fp8bs.fp8bs_gemm_bf16a(Xp, qa, sa, qw, sw, out,
+                                                                            fp8bs.OUT_BF16))
+        rows[f"bf16a_projection_{N}"] = {
+            "shape": f"M{M} N{N} K{K}",
+            "us_quant_act": t_q * 1e3, "us_gemm": t_g * 1e3, "us_quant_act_then_gemm": t_p * 1e3,
+            "us_gemm_bf16a": t_a * 1e3, "us_gemm_bf16a_with_codes": t_c * 1e3,
+            "speedup_vs_pair": t_p / t_a, "speedup_with_codes_vs_pair": t_p / t_c,
+            "TFLOP/s_gemm_bf16a": fl / t_a / 1e9, "TFLOP/s_pair": fl / t_p / 1e9,
+            "timing": f"medians, each call after a {FLUSH_BYTES >> 30} GiB cache flush"}
+        del Wp, qw, sw, out
+    del Xp, qa, sa
     # every row: median as "us" (the rates above), plus mean and min, all
     # measured after a cache flush
     timer_of = {"requant_T_128x1_fp8": "requant_fp8", "requant_T_128x1_bf16": "requant_bf16",

@@ -275,6 +275,33 @@ fp8bs_status fp8bs_gemm_quant_1x128(const uint8_t* a, const float* sa, int64_t l
                                      static_cast<hipStream_t>(stream)));
 }
 
+fp8bs_status fp8bs_gemm_bf16a(const void* x, int64_t ldx, uint8_t* qx, int64_t ldqx, float* sx,
+                              int64_t ldsx, const uint8_t* b, const float* sb, int64_t ldb, int64_t ldsb,
+                              void* d, int64_t ldd, fp8bs_out_dtype dt, int64_t M, int64_t N, int64_t K,
+                              void* stream) {
+  if (dt != FP8BS_OUT_BF16 && dt != FP8BS_OUT_F32) return FP8BS_ERR_INVALID_ARG;
+  if (M < 0 || N < 0 || K <= 0) return FP8BS_ERR_INVALID_ARG;
+  if (K % 128 != 0) return FP8BS_ERR_UNSUPPORTED_SHAPE;
+  if ((qx == nullptr) != (sx == nullptr)) return FP8BS_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  FP8BS_TRY(check_matrix(x, K, ldx, 2));
+  FP8BS_TRY(check_matrix(b, K, ldb, 1));
+  FP8BS_TRY(check_scales(sb, K / 128, ldsb));
+  FP8BS_TRY(check_matrix(d, N, ldd, dt == FP8BS_OUT_F32 ? 4 : 2));
+  if (qx != nullptr) {
+    FP8BS_TRY(check_matrix(qx, K, ldqx, 1));
+    FP8BS_TRY(check_scales(sx, K / 128, ldsx));
+  }
+  // 64-row tiles of bf16 A and 256-row tiles of codes are addressed with
+  // 32-bit offsets from their first row
+  if (ldx >= kMaxCodeStride / 2 || ldb >= kMaxCodeStride || ldsb >= kMaxScaleStride)
+    return FP8BS_ERR_UNSUPPORTED_SHAPE;
+  FP8BS_TRY(check_device());
+  return launched(fp8bs::launch_gemm_bf16a(static_cast<const uint16_t*>(x), ldx, qx, ldqx, sx, ldsx, b, sb,
+                                           ldb, ldsb, d, ldd, dt == FP8BS_OUT_F32, M, N, K,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 fp8bs_status fp8bs_grouped_gemm(const uint8_t* a, const float* sa, int64_t ldsa,
                                 const uint8_t* b, const float* sb,
                                 const int32_t* offsets, int32_t E, int64_t M_total,

@@ -44,6 +44,11 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t l
                        bool bscale_row, void* d, int64_t ldd, float* s_out, int64_t lds_out,
                        int out, int64_t M, int64_t N, int64_t K, hipStream_t st);
 
+hipError_t launch_gemm_bf16a(const uint16_t* x, int64_t ldx, uint8_t* qx, int64_t ldqx, float* sx,
+                             int64_t ldsx, const uint8_t* b, const float* sb, int64_t ldb, int64_t ldsb,
+                             void* d, int64_t ldd, bool out_f32, int64_t M, int64_t N, int64_t K,
+                             hipStream_t st);
+
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, int64_t ldsa,
                                const uint8_t* b, const float* sb, const int32_t* offsets,
                                int32_t E, int64_t M_total, void* d, bool out_f32,

@@ -35,7 +35,7 @@ ENTRY_POINTS = ("fp8bs_quant_act_1x128", "fp8bs_quant_w_128x128", "fp8bs_quant_a
                 "fp8bs_quant_per_tensor",
                 "fp8bs_cast_e4m3",
                 "fp8bs_encode_e5m6", "fp8bs_decode_e5m6", "fp8bs_requant_T_128x1",
-                "fp8bs_transpose_w_128x128", "fp8bs_gemm", "fp8bs_gemm_quant_1x128",
+                "fp8bs_transpose_w_128x128", "fp8bs_gemm", "fp8bs_gemm_quant_1x128", "fp8bs_gemm_bf16a",
                 "fp8bs_grouped_gemm",
                 "fp8bs_status_string", "fp8bs_version")
 
@@ -82,6 +82,7 @@ def load() -> ctypes.CDLL:
         "fp8bs_gemm": [P, P, I64, I64, P, P, I64, I64, I, P, I64, I, I64, I64, I64, P],
         "fp8bs_gemm_quant_1x128": [P, P, I64, I64, P, P, I64, I64, I, P, I64, P, I64, I64, I64, I64, P],
         "fp8bs_grouped_gemm": [P, P, I64, P, P, P, I32, I64, P, I, I64, I64, P],
+        "fp8bs_gemm_bf16a": [P, I64, P, I64, P, I64, P, P, I64, I64, P, I64, I, I64, I64, I64, P],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -288,6 +289,26 @@ def fp8bs_gemm_quant_1x128(a, sa, b, sb, bmode, q, s, stream=None):
           _ld(sb), int(bmode), _ptr(q), _ld(q), _ptr(s), _ld(s), M, N, K, _stream(stream))
 
 
+def fp8bs_gemm_bf16a(x, qx, sx, b, sb, d, dt, stream=None):
+    """D [M][N] = quant_1x128(x bf16 [M][K]) * B [N][K]^T with 128x128 B
+    scales; qx u8 [M][K] and sx f32 [M][K/128] receive the codes of x when
+    given (both or neither)."""
+    M, K = x.shape
+    N = b.shape[0]
+    _check(x, "x", (M, K), ("bfloat16",))
+    if (qx is None) != (sx is None):
+        raise ValueError("qx and sx: both or neither")
+    if qx is not None:
+        _check(qx, "qx", (M, K), _CODES)
+        _check(sx, "sx", (M, (">=", _groups(K))), ("float32",))
+    _check(b, "b", (N, K), _CODES)
+    _check(sb, "sb", ((N + 127) // 128, (">=", _groups(K))), ("float32",))
+    _check(d, "d", (M, N), ("float32",) if int(dt) == OUT_F32 else ("bfloat16",))
+    _call("fp8bs_gemm_bf16a", _ptr(x), _ld(x), _ptr(qx), _ld(qx) if qx is not None else 0, _ptr(sx),
+          _ld(sx) if sx is not None else 0, _ptr(b), _ptr(sb), _ld(b), _ld(sb), _ptr(d), _ld(d), int(dt),
+          M, N, K, _stream(stream))
+
+
 def fp8bs_grouped_gemm(a, sa, b, sb, offsets, d, dt, stream=None):
     """Per-expert D rows = A rows * B[e]^T; offsets int32 [E+1] on the device."""
     M_total, K = a.shape
@@ -410,6 +431,19 @@ def gemm_quant_1x128(a, sa, b, sb, bmode=BSCALE_BLOCK_128x128, stream=None):
     s = torch.empty((M, N // 128), dtype=torch.float32, device=a.device)
     fp8bs_gemm_quant_1x128(a, sa, b, sb, bmode, q, s, stream)
     return q, s
+
+
+def gemm_bf16a(x, b, sb, out_f32=False, with_codes=False, stream=None):
+    import torch
+    M, K = x.shape
+    N = b.shape[0]
+    d = torch.empty((M, N), dtype=torch.float32 if out_f32 else torch.bfloat16, device=x.device)
+    qx = sx = None
+    if with_codes:
+        qx = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        sx = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    fp8bs_gemm_bf16a(x, qx, sx, b, sb, d, OUT_F32 if out_f32 else OUT_BF16, stream)
+    return (d, qx, sx) if with_codes else d
 
 
 def grouped_gemm(a, sa, b, sb, offsets, out_f32=False, stream=None):

@@ -247,6 +247,29 @@ fp8bs_status fp8bs_gemm_quant_1x128(const uint8_t *a, const float *sa, int64_t l
                                     int64_t lds, int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
+ * Block-scaled FP8 GEMM whose A operand is given in BF16 and quantized in
+ * 1x128 tiles inside the GEMM, so the FP8 activation never crosses HBM
+ * ([p2] para 1 describes the HBM round trip of separate quantization: BF16
+ * read, FP8 written back, read again for the MMA).  Each tile of A is
+ * quantized exactly as fp8bs_quant_act_1x128 quantizes it ([p1] para 3)
+ * and D is then computed as by fp8bs_gemm on those codes with 128x128 B
+ * scales (bit for bit the same D).  Each 64-row tile of A is quantized once
+ * per 256-column tile of B, so the form is meant for small N.
+ *   x   bf16 [M][ldx]          A
+ *   qx  u8   [M][ldqx] or NULL the E4M3 codes of A are also stored (the FP8
+ *   sx  f32  [M][ldsx] or NULL activation cache for the backward pass);
+ *                              both given or both NULL
+ *   b, sb, ldb, ldsb           as for fp8bs_gemm with FP8BS_BSCALE_BLOCK_128x128
+ *   d   bf16 or f32 [M][ldd]
+ * M, N >= 0 (either 0 is a no-op), K > 0, K % 128 == 0; ldx < 2^23,
+ * ldb < 2^24, ldsb < 2^22, else FP8BS_ERR_UNSUPPORTED_SHAPE.
+ */
+fp8bs_status fp8bs_gemm_bf16a(const void *x, int64_t ldx, uint8_t *qx, int64_t ldqx, float *sx,
+                              int64_t ldsx, const uint8_t *b, const float *sb, int64_t ldb,
+                              int64_t ldsb, void *d, int64_t ldd, fp8bs_out_dtype dt, int64_t M,
+                              int64_t N, int64_t K, void *stream);
+
+/*
  * Grouped block-scaled GEMM for the experts one GPU holds, with ragged
  * token counts (the per-expert FP8 GEMMs of the MoE layers; [p2] para 2).
  * Rows offsets[e] .. offsets[e+1]-1 of A are multiplied by expert e:

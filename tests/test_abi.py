@@ -82,6 +82,12 @@ def gemm_quant(a=A, sa=A, lda=256, ldsa=2, b=A, sb=A, ldb=256, ldsb=2, bmode=0, 
                                                M, N, K, NULL)
 
 
+def gemm_bf16a(x=A, ldx=256, qx=A, ldqx=256, sx=A, ldsx=2, b=A, sb=A, ldb=256, ldsb=2, d=A, ldd=64, dt=0,
+               M=8, N=64, K=256):
+    return fp8bs.load().fp8bs_gemm_bf16a(x, ldx, qx, ldqx, sx, ldsx, b, sb, ldb, ldsb, d, ldd, dt, M, N, K,
+                                         NULL)
+
+
 def grouped(a=A, sa=A, ldsa=2, b=A, sb=A, off=A, E=2, M=10, d=A, dt=0, N=128, K=256):
     return fp8bs.load().fp8bs_grouped_gemm(a, sa, ldsa, b, sb, off, E, M, d, dt, N, K, NULL)
 
@@ -187,6 +193,23 @@ def grouped(a=A, sa=A, ldsa=2, b=A, sb=A, off=A, E=2, M=10, d=A, dt=0, N=128, K=
     (lambda: gemm(ldsb=1 << 22), fp8bs.ERR_UNSUPPORTED_SHAPE),
     (lambda: gemm(M=0), fp8bs.OK),
     (lambda: gemm(N=0), fp8bs.OK),
+    (lambda: gemm_bf16a(dt=5), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm_bf16a(K=192, ldx=256, ldb=256, ldqx=256), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: gemm_bf16a(M=-1), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm_bf16a(x=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm_bf16a(qx=NULL), fp8bs.ERR_INVALID_ARG),             # codes without scales
+    (lambda: gemm_bf16a(sx=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm_bf16a(ldx=128), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm_bf16a(ldsx=1), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm_bf16a(ldsb=1), fp8bs.ERR_INVALID_ARG),
+    (lambda: gemm_bf16a(x=A + 8), fp8bs.ERR_MISALIGNED),
+    (lambda: gemm_bf16a(ldx=260), fp8bs.ERR_MISALIGNED),
+    (lambda: gemm_bf16a(ldqx=264), fp8bs.ERR_MISALIGNED),
+    (lambda: gemm_bf16a(ldd=68), fp8bs.ERR_MISALIGNED),
+    (lambda: gemm_bf16a(ldx=1 << 23), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: gemm_bf16a(ldb=1 << 24), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: gemm_bf16a(M=0), fp8bs.OK),
+    (lambda: gemm_bf16a(N=0, qx=NULL, sx=NULL), fp8bs.OK),
     (lambda: gemm_quant(bmode=3), fp8bs.ERR_INVALID_ARG),
     (lambda: gemm_quant(N=192, ldq=192, lds=2), fp8bs.ERR_UNSUPPORTED_SHAPE),
     (lambda: gemm_quant(K=200, lda=256, ldb=256), fp8bs.ERR_UNSUPPORTED_SHAPE),
@@ -301,6 +324,28 @@ def test_binding_refuses_mismatched_outputs():
         fp8bs.fp8bs_requant_T_128x1(fp8bs.SRC_FP8_1x128, xq, torch.zeros((256, 3), dtype=torch.float32),
                                     torch.zeros((256, 384), dtype=torch.uint8),
                                     torch.zeros((384, 2), dtype=torch.float32), stream=0)
+
+
+def test_binding_refuses_mismatched_bf16a_operands():
+    import torch
+    x = torch.zeros((100, 256), dtype=torch.bfloat16)
+    qx = torch.zeros((100, 256), dtype=torch.uint8)
+    sx = torch.zeros((100, 2), dtype=torch.float32)
+    b = torch.zeros((300, 256), dtype=torch.uint8)
+    sb = torch.zeros((3, 2), dtype=torch.float32)
+    d = torch.zeros((100, 300), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="both or neither"):
+        fp8bs.fp8bs_gemm_bf16a(x, qx, None, b, sb, d, fp8bs.OUT_BF16, stream=0)
+    with pytest.raises(ValueError, match="dimension 0"):
+        fp8bs.fp8bs_gemm_bf16a(x, qx[:99], sx, b, sb, d, fp8bs.OUT_BF16, stream=0)
+    with pytest.raises(ValueError, match="dimension 0"):
+        fp8bs.fp8bs_gemm_bf16a(x, qx, sx, b, sb[:2], d, fp8bs.OUT_BF16, stream=0)
+    with pytest.raises(ValueError, match="dtype"):
+        fp8bs.fp8bs_gemm_bf16a(x.float(), qx, sx, b, sb, d, fp8bs.OUT_BF16, stream=0)
+    with pytest.raises(ValueError, match="dtype"):
+        fp8bs.fp8bs_gemm_bf16a(x, qx, sx, b, sb, d, fp8bs.OUT_F32, stream=0)
+    with pytest.raises(ValueError, match="dimension 1"):
+        fp8bs.fp8bs_gemm_bf16a(x, qx, sx, b, sb, d[:, :299], fp8bs.OUT_BF16, stream=0)
 
 
 def test_binding_refuses_host_tensors():
