@@ -6,7 +6,9 @@ stage read before its copy, an unwritten tail) would then produce NaNs or
 wrong codes.  These parity cases run through that build and must still
 match the oracle exactly as the library build does: ragged and strided
 shapes, both B-scale modes, every output form, requant from both sources,
-the weight transpose and the grouped GEMM with empty experts.
+the weight transpose, the grouped GEMM with empty experts, the BF16-A GEMM
+(A quantized in place in LDS) and the one-launch activation and weight
+quantizer.
 """
 import os
 
@@ -102,3 +104,27 @@ def test_transpose_and_quant_w_poisoned():
     check_quant_equal("poisoned quant_w", host(qg), host(sg), q, s)
     qt, st = _transpose_dev(q, s, pad_q=16, pad_s=3, pad_qt=32, pad_st=2)
     check_quant_equal("poisoned transpose_w", qt, st, *oracle.transpose_w_128x128(q, s))
+
+
+@pytest.mark.parametrize("M,N,K", [(129, 264, 640), (300, 576, 128)])
+def test_gemm_bf16a_poisoned(M, N, K):
+    """The BF16-A GEMM quantizes A in place in its raw LDS stages and keeps
+    the scales in the rows' free chunks: every code, scale and B stage it
+    reads must have been written first."""
+    from tests.test_gpu_gemm_bf16a import _full
+    native_loaded()
+    q = synth.tiny(M=M, N=N, K=K, seed=M + 5 * N)
+    announce(f"poisoned gemm_bf16a {M}x{N}x{K}")
+    _full(f"poisoned bf16a {M}x{N}x{K}", q["A"], q["W"], pads=(8, 16, 3, 8))
+
+
+def test_quant_act_w_poisoned():
+    from tests.test_gpu_quant import _run_act_w
+    native_loaded()
+    rng = np.random.default_rng(5)
+    x = synth.bf16_bits(rng.standard_normal((70, 384)).astype(np.float32))
+    w = synth.bf16_bits(rng.standard_normal((300, 384)).astype(np.float32))
+    announce("poisoned quant_act_w 70x384 + 300x384")
+    qx, sx, qw, sw = _run_act_w(x, w, pad=16)
+    check_quant_equal("poisoned quant_act_w activation", qx, sx, *oracle.quant_act_1x128(x))
+    check_quant_equal("poisoned quant_act_w weight", qw, sw, *oracle.quant_w_128x128(w))
