@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--profile-kernel", choices=["quant_act", "quant_w", "quant_act_w", "gemm"],
+                    help="only run this kernel of the step --steps times on the step's inputs "
+                         "(for counter runs); prints no JSON line")
     return ap.parse_args()
 
 
@@ -450,6 +453,21 @@ def main():
     qw = torch.empty((N, K), dtype=torch.uint8, device=dev)
     sw = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    if args.profile_kernel:
+        calls = {
+            "quant_act": lambda: fp8bs.fp8bs_quant_act_1x128(X, qx, sx),
+            "quant_w": lambda: fp8bs.fp8bs_quant_w_128x128(W, qw, sw),
+            "quant_act_w": lambda: fp8bs.fp8bs_quant_act_w(X, qx, sx, W, qw, sw),
+            "gemm": lambda: fp8bs.fp8bs_gemm(qx, sx, qw, sw, fp8bs.BSCALE_BLOCK_128x128, Y, fp8bs.OUT_BF16),
+        }
+        if args.profile_kernel == "gemm":
+            fp8bs.fp8bs_quant_act_w(X, qx, sx, W, qw, sw)
+        for _ in range(args.steps):
+            calls[args.profile_kernel]()
+        torch.cuda.synchronize()
+        log(f"ran {args.profile_kernel} {args.steps} times")
+        return
 
     kt = KernelTimer()
 

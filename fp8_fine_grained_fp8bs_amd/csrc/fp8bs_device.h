@@ -140,21 +140,38 @@ __device__ __noinline__ uint32_t encode_general(float x, float s) {
   return resolve_pair(xs, ss, clo, chi);
 }
 
+// Repair of a word whose brackets differ somewhere (s >= 2^-100), without
+// branches: in every byte the midpoint mu of the two codes' magnitudes
+// (exact: adjacent E4M3 values sum exactly) decides by the exact sign of
+// |x| - mu s = fma(-(dec(lo) + dec(hi)), s / 2, |x|); the upper code is
+// taken where that is positive, or zero with an odd lower code (ties to
+// even).  Bytes whose brackets agree keep lo.  The sign test reads the FP32
+// bits as an integer: positive > 0, +0 = 0, negative < 0 (an exact zero
+// from the fma is +0).
+__device__ __forceinline__ uint32_t repair_word(const float v[4], float s, uint32_t lo, uint32_t hi) {
+  const int mlo = static_cast<int>(lo & 0x7f7f7f7fu), mhi = static_cast<int>(hi & 0x7f7f7f7fu);
+  const auto l01 = __builtin_amdgcn_cvt_pk_f32_fp8(mlo, false), l23 = __builtin_amdgcn_cvt_pk_f32_fp8(mlo, true);
+  const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(mhi, false), h23 = __builtin_amdgcn_cvt_pk_f32_fp8(mhi, true);
+  const float sum[4] = {l01[0] + h01[0], l01[1] + h01[1], l23[0] + h23[0], l23[1] + h23[1]};
+  const float hs = 0.5f * s;
+  uint32_t up = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float t = __builtin_fmaf(-sum[i], hs, __builtin_fabsf(v[i]));
+    const int key = __float_as_int(t) + static_cast<int>((lo >> (8 * i)) & 1u);
+    up |= (key > 0 ? 1u : 0u) << (8 * i);
+  }
+  return lo + ((lo ^ hi) & 0x01010101u & up);
+}
+
 // Encode 4 values with one tile's constants; returns the packed codes.
-// Fast path when the brackets agree; per-byte repair otherwise.
+// Fast path when the brackets agree; the word's repair otherwise.
 __device__ __forceinline__ uint32_t encode4(const float v[4], const TileScale& t) {
   if (t.fast) {
     const uint32_t lo = cvt4(v[0] * t.rlo, v[1] * t.rlo, v[2] * t.rlo, v[3] * t.rlo);
     const uint32_t hi = cvt4(v[0] * t.rhi, v[1] * t.rhi, v[2] * t.rhi, v[3] * t.rhi);
     if (__builtin_expect(lo == hi, 1)) return lo;
-    uint32_t out = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t cl = (lo >> (8 * i)) & 0xffu, ch = (hi >> (8 * i)) & 0xffu;
-      const uint32_t c = (cl == ch) ? cl : resolve_pair(v[i], t.s, cl, ch);
-      out |= c << (8 * i);
-    }
-    return out;
+    return repair_word(v, t.s, lo, hi);
   }
   uint32_t out = 0;
 #pragma unroll
