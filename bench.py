@@ -376,6 +376,32 @@ def time_rows(dev, reps=20, warm=3):
         rows[f"grouped_gemm_{tag}"] = {"shape": f"E{E} sumM{Ttok} N{N} K{K}", "us": ms * 1e3,
                                        "TFLOP/s": fl / ms / 1e9, "frac_fp8_peak": fl / ms / 1e9 / FP8_PEAK_TFLOPS}
         del A, Wt, qa, sa, qw, sw, out
+    # SwiGLU of the MoE up-projection's halves, quantized 1x128 for the down
+    # projection (16384 tokens x 2048), fused against SwiGLU to BF16 then
+    # quant_act
+    log("rows: swiglu quantization")
+    gen = torch.Generator(device=dev).manual_seed(7)
+    Ttok, I = 16384, 2048
+    gu = (torch.randn((Ttok, 2 * I), generator=gen, device=dev) * 1.5).to(torch.bfloat16)
+    gs, us = gu[:, :I], gu[:, I:]
+    qs = torch.empty((Ttok, I), dtype=torch.uint8, device=dev)
+    ss = torch.empty((Ttok, I // 128), dtype=torch.float32, device=dev)
+    hs = torch.empty((Ttok, I), dtype=torch.bfloat16, device=dev)
+    t_f = timed("swiglu_fused", lambda: fp8bs.fp8bs_swiglu_quant_1x128(gs, us, qs, ss, None))
+
+    def swiglu_unfused():
+        fp8bs.fp8bs_swiglu_quant_1x128(gs, us, None, None, hs)
+        fp8bs.fp8bs_quant_act_1x128(hs, qs, ss)
+    t_u = timed("swiglu_unfused", swiglu_unfused)
+    n_el = Ttok * I
+    b_f = n_el * (2 + 2 + 1) + Ttok * (I // 128) * 4
+    rows["swiglu_quant_1x128"] = {"shape": f"g, u [{Ttok}][{I}] (halves of [{Ttok}][{2 * I}])",
+                                  "us": t_f * 1e3, "GB/s": b_f / t_f / 1e6,
+                                  "frac_hbm": b_f / t_f / 1e6 / HBM_PEAK_GBS, "bytes": b_f,
+                                  "us_unfused_bf16_h_then_quant_act": t_u * 1e3,
+                                  "speedup_vs_unfused": t_u / t_f}
+    del gu, gs, us, qs, ss, hs
+
     # BF16 A quantized inside the GEMM (the FP8 activation never crosses HBM)
     # against quant_act + gemm, on the low-rank projections 7168 -> 576 and
     # 7168 -> 1536 of 4096 tokens (small N: A is re-quantized per 256-column
@@ -415,7 +441,8 @@ def time_rows(dev, reps=20, warm=3):
     # measured after a cache flush
     timer_of = {"requant_T_128x1_fp8": "requant_fp8", "requant_T_128x1_bf16": "requant_bf16",
                 "encode_e5m6": "e5m6_enc", "decode_e5m6": "e5m6_dec", "gemm_wgrad_row_f32": "wgrad",
-                "transpose_w_128x128": "transpose_w", "gemm_dgrad_bf16": "dgrad"}
+                "transpose_w_128x128": "transpose_w", "gemm_dgrad_bf16": "dgrad",
+                "swiglu_quant_1x128": "swiglu_fused"}
     for tag in ("up", "down"):
         timer_of.update({f"quant_act_moe_{tag}": f"qa_{tag}", f"quant_w_moe_{tag}": f"qw_{tag}",
                          f"grouped_gemm_{tag}": f"grouped_{tag}"})

@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8bs.so")
 # debug build for race checks: kernels fill their LDS with 0xFF before use
 POISON_LIB = os.path.join(PKG, "libfp8bs_poison.so")
-SOURCES = ["api.hip", "quant.hip", "requant.hip", "gemm.hip", "gemm_bf16a.hip", "e5m6.hip"]
+SOURCES = ["api.hip", "quant.hip", "requant.hip", "gemm.hip", "gemm_bf16a.hip", "e5m6.hip", "swiglu.hip"]
 LDS_SOURCES = ["quant.hip", "requant.hip", "gemm.hip", "gemm_bf16a.hip"]   # the sources whose kernels use LDS
 ARCH = "gfx950"
 

@@ -187,6 +187,28 @@ fp8bs_status fp8bs_decode_e5m6(const uint8_t* y, int64_t T, int64_t C, int64_t l
                                             static_cast<hipStream_t>(stream)));
 }
 
+fp8bs_status fp8bs_swiglu_quant_1x128(const void* g, int64_t ldg, const void* u, int64_t ldu,
+                                      int64_t T, int64_t I, uint8_t* q, int64_t ldq, float* s,
+                                      int64_t lds, void* h, int64_t ldh, void* stream) {
+  if (T < 0 || I <= 0) return FP8BS_ERR_INVALID_ARG;
+  if (I % 128 != 0) return FP8BS_ERR_UNSUPPORTED_SHAPE;
+  if ((q == nullptr) != (s == nullptr)) return FP8BS_ERR_INVALID_ARG;
+  if (q == nullptr && h == nullptr) return FP8BS_ERR_INVALID_ARG;
+  if (T == 0) return FP8BS_OK;
+  FP8BS_TRY(check_matrix(g, I, ldg, 2));
+  FP8BS_TRY(check_matrix(u, I, ldu, 2));
+  if (q != nullptr) {
+    FP8BS_TRY(check_matrix(q, I, ldq, 1));
+    FP8BS_TRY(check_scales(s, I / 128, lds));
+  }
+  if (h != nullptr) FP8BS_TRY(check_matrix(h, I, ldh, 2));
+  FP8BS_TRY(check_device());
+  return launched(fp8bs::launch_swiglu_quant_1x128(static_cast<const uint16_t*>(g), ldg,
+                                                   static_cast<const uint16_t*>(u), ldu, T, I, q, ldq, s,
+                                                   lds, static_cast<uint16_t*>(h), ldh,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 fp8bs_status fp8bs_requant_T_128x1(fp8bs_requant_src src, const void* in, const float* s_in,
                                    int64_t T, int64_t C, int64_t ld_in, int64_t lds_in,
                                    uint8_t* q_out, int64_t ld_out, float* s_out, int64_t lds_out,

@@ -21,6 +21,10 @@ hipError_t launch_quant_act_w(const uint16_t* x, int64_t M, int64_t ldx, uint8_t
 
 hipError_t launch_cast_e4m3(const float* x, int64_t n, uint8_t* q, hipStream_t st);
 
+hipError_t launch_swiglu_quant_1x128(const uint16_t* g, int64_t ldg, const uint16_t* u, int64_t ldu,
+                                     int64_t T, int64_t I, uint8_t* q, int64_t ldq, float* s,
+                                     int64_t lds, uint16_t* h, int64_t ldh, hipStream_t st);
+
 hipError_t launch_quant_per_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* s,
                                    hipStream_t st);
 

@@ -32,6 +32,7 @@ SRC_FP8_1x128 = 0
 SRC_BF16 = 1
 
 ENTRY_POINTS = ("fp8bs_quant_act_1x128", "fp8bs_quant_w_128x128", "fp8bs_quant_act_w",
+                "fp8bs_swiglu_quant_1x128",
                 "fp8bs_quant_per_tensor",
                 "fp8bs_cast_e4m3",
                 "fp8bs_encode_e5m6", "fp8bs_decode_e5m6", "fp8bs_requant_T_128x1",
@@ -71,6 +72,7 @@ def load() -> ctypes.CDLL:
     P, I64, I32, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
     sigs = {
         "fp8bs_quant_act_1x128": [P, I64, I64, I64, P, I64, P, I64, P],
+        "fp8bs_swiglu_quant_1x128": [P, I64, P, I64, I64, I64, P, I64, P, I64, P, I64, P],
         "fp8bs_quant_w_128x128": [P, I64, I64, I64, P, I64, P, I64, P],
         "fp8bs_quant_act_w": [P, I64, I64, P, I64, P, I64, P, I64, I64, P, I64, P, I64, I64, P],
         "fp8bs_quant_per_tensor": [P, I64, P, P, P],
@@ -358,6 +360,36 @@ def fp8bs_quant_act_w(x, qx, sx, w, qw, sw, stream=None):
     _check(sw, "sw", ((N + 127) // 128, (">=", _groups(K))), ("float32",))
     _call("fp8bs_quant_act_w", _ptr(x), M, _ld(x), _ptr(qx), _ld(qx), _ptr(sx), _ld(sx),
           _ptr(w), N, _ld(w), _ptr(qw), _ld(qw), _ptr(sw), _ld(sw), K, _stream(stream))
+
+
+def fp8bs_swiglu_quant_1x128(g, u, q, s, h, stream=None):
+    """h = silu(g) u of bf16 [T][I] halves -> q u8 [T][I] + s f32 [T][I/128]
+    (1x128 tiles; both or neither) and/or h bf16 [T][I]."""
+    T, I = g.shape
+    _check(g, "g", (T, I), ("bfloat16",))
+    _check(u, "u", (T, I), ("bfloat16",))
+    if (q is None) != (s is None):
+        raise ValueError("q and s: both or neither")
+    if q is None and h is None:
+        raise ValueError("no output")
+    if q is not None:
+        _check(q, "q", (T, I), _CODES)
+        _check(s, "s", (T, (">=", _groups(I))), ("float32",))
+    if h is not None:
+        _check(h, "h", (T, I), ("bfloat16",))
+    _call("fp8bs_swiglu_quant_1x128", _ptr(g), _ld(g), _ptr(u), _ld(u), T, I, _ptr(q),
+          _ld(q) if q is not None else 0, _ptr(s), _ld(s) if s is not None else 0, _ptr(h),
+          _ld(h) if h is not None else 0, _stream(stream))
+
+
+def swiglu_quant_1x128(g, u, with_h=False, stream=None):
+    import torch
+    T, I = g.shape
+    q = torch.empty((T, I), dtype=torch.uint8, device=g.device)
+    s = torch.empty((T, I // 128), dtype=torch.float32, device=g.device)
+    h = torch.empty((T, I), dtype=torch.bfloat16, device=g.device) if with_h else None
+    fp8bs_swiglu_quant_1x128(g, u, q, s, h, stream)
+    return (q, s, h) if with_h else (q, s)
 
 
 def quant_act_w(x, w, stream=None):

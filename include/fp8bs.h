@@ -159,6 +159,32 @@ fp8bs_status fp8bs_decode_e5m6(const uint8_t *y, int64_t T, int64_t C, int64_t l
                                int64_t ldx, void *stream);
 
 /*
+ * SwiGLU of the cached gate and up halves, quantized for the down-projection.
+ * [p1] para 4 and [p4] para 3 cache the inputs of the SwiGLU operator and
+ * recompute its output in the backward pass; [p1] para 3 quantizes a GEMM
+ * input in 1x128 tiles along its K (here I); [p2] para 1 counts the HBM
+ * round trip that a separate quantization costs.
+ *   h = silu(g) * u = g * u / (1 + e^-g), computed in FP32 (within a few
+ *   units in the last place of the exact value where it is normal)
+ *   g, u  bf16 [T][ldg], [T][ldu]   the two halves (a [T][2I] up-projection
+ *                                   output: u = g + I, ldu = ldg)
+ *   q, s  u8 [T][ldq], f32 [T][lds] E4M3 codes and 1x128 scales of h,
+ *                                   s = fl32(amax / 448), codes the
+ *                                   nearest-even E4M3 of h / s (as
+ *                                   fp8bs_quant_act_1x128 quantizes FP32
+ *                                   values); both or neither
+ *   h     bf16 [T][ldh] or NULL     h rounded to nearest-even BF16 (the
+ *                                   backward pass's recompute)
+ * At least one output.  T >= 0 (0 is a no-op), I > 0 and I % 128 == 0, else
+ * FP8BS_ERR_INVALID_ARG / FP8BS_ERR_UNSUPPORTED_SHAPE; buffers and row
+ * strides 16-byte aligned.  NaN and infinite inputs are outside the
+ * contract.
+ */
+fp8bs_status fp8bs_swiglu_quant_1x128(const void *g, int64_t ldg, const void *u, int64_t ldu,
+                                      int64_t T, int64_t I, uint8_t *q, int64_t ldq, float *s,
+                                      int64_t lds, void *h, int64_t ldh, void *stream);
+
+/*
  * Backward re-quantization of 1x128 tiles into 128x1 tiles, transposed.
  * [p1] para 3: in the backward pass the activation tiles are converted
  * from 1x128 to 128x1; [p1] para 4: activations are cached in FP8 for the

@@ -67,6 +67,7 @@ def _load():
         "orc_quant_act_1x128": (None, [P, I64, I64, P, P]),
         "orc_quant_act_1x128_f32": (None, [P, I64, I64, P, P]),
         "orc_quant_w_128x128": (None, [P, I64, I64, P, P]),
+        "orc_swiglu_quant_1x128": (None, [P, P, I64, I64, P, P, P, P]),
         "orc_requant_T_128x1": (None, [ctypes.c_int, P, P, I64, I64, P, P]),
         "orc_gemm": (None, [P, P, P, P, ctypes.c_int, I64, I64, I64, P]),
         "orc_gemm_entries": (None, [P, P, P, P, ctypes.c_int, I64, P, P, I64, P]),
@@ -180,6 +181,26 @@ def quant_act_1x128_f32(x_f32: np.ndarray):
     s = np.empty((M, K // 128), np.float32)
     _load().orc_quant_act_1x128_f32(_p(x), M, K, _p(q), _p(s))
     return q, s
+
+
+def swiglu_quant_1x128(g_bf16: np.ndarray, u_bf16: np.ndarray):
+    """SwiGLU of the cached gate and up halves ([p1] para 4, [p4] para 3:
+    the SwiGLU inputs are cached and its output recomputed), h = silu(g) u
+    in binary64 rounded once to binary32, then 1x128 tiles along I as in
+    quant_act_1x128_f32 ([p1] para 3).  g, u bf16 [T][I] -> (codes [T][I],
+    scales [T][I/128], h binary32 [T][I], h bf16 bits [T][I] rounded once
+    from binary64)."""
+    g = _u16(g_bf16)
+    u = _u16(u_bf16)
+    assert g.shape == u.shape
+    T, I = g.shape
+    assert I % 128 == 0
+    q = np.empty((T, I), np.uint8)
+    s = np.empty((T, I // 128), np.float32)
+    h32 = np.empty((T, I), np.float32)
+    h16 = np.empty((T, I), np.uint16)
+    _load().orc_swiglu_quant_1x128(_p(g), _p(u), T, I, _p(q), _p(s), _p(h32), _p(h16))
+    return q, s, h32, h16
 
 
 def quant_w_128x128(w_bf16: np.ndarray):

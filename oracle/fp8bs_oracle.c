@@ -227,6 +227,38 @@ void orc_quant_act_1x128_f32(const float *x, int64_t M, int64_t K,
     }
 }
 
+/* SwiGLU of the cached gate and up halves, quantized for the
+ * down-projection.  [p1] para 4 and [p4] para 3 cache the inputs of the
+ * SwiGLU operator (recomputing its output in the backward pass); [p1]
+ * para 3 quantizes the input of a GEMM in 1x128 tiles along its K.
+ * Reading taken: h = silu(g) * u with silu(g) = g / (1 + e^-g), evaluated
+ * in binary64 (libm exp) and rounded once to binary32; the binary32 rows
+ * are then quantized exactly as orc_quant_act_1x128_f32 quantizes them.
+ * g, u: bf16 [T][I]; q: [T][I]; s: [T][I/128]; h32: [T][I] (the rounded
+ * h, for the tests); h16: [T][I] bf16 bits of h rounded once from
+ * binary64, or NULL. */
+static double silu_times(double g, double u)
+{
+    return g / (1.0 + exp(-g)) * u;
+}
+
+void orc_swiglu_quant_1x128(const uint16_t *g, const uint16_t *u, int64_t T,
+                            int64_t I, uint8_t *q, float *s, float *h32,
+                            uint16_t *h16)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t i = 0; i < I; ++i) {
+            double h = silu_times(orc_bf16_value(g[t * I + i]),
+                                  orc_bf16_value(u[t * I + i]));
+            h32[t * I + i] = (float)h;
+            if (h16)
+                h16[t * I + i] = orc_bf16_round(h);
+        }
+    }
+    orc_quant_act_1x128_f32(h32, T, I, q, s);
+}
+
 /* Weight quantization, 128x128 blocks.
  * w: bf16 [N][K] (ld = K); q: [N][K]; s: [ceil(N/128)][K/128].
  * A partial last block row takes its amax over the rows present. */

@@ -88,6 +88,10 @@ def gemm_bf16a(x=A, ldx=256, qx=A, ldqx=256, sx=A, ldsx=2, b=A, sb=A, ldb=256, l
                                          NULL)
 
 
+def swiglu(g=A, ldg=256, u=A, ldu=256, T=4, I=256, q=A, ldq=256, s=A, lds=2, h=A, ldh=256):
+    return fp8bs.load().fp8bs_swiglu_quant_1x128(g, ldg, u, ldu, T, I, q, ldq, s, lds, h, ldh, NULL)
+
+
 def grouped(a=A, sa=A, ldsa=2, b=A, sb=A, off=A, E=2, M=10, d=A, dt=0, N=128, K=256):
     return fp8bs.load().fp8bs_grouped_gemm(a, sa, ldsa, b, sb, off, E, M, d, dt, N, K, NULL)
 
@@ -193,6 +197,17 @@ def grouped(a=A, sa=A, ldsa=2, b=A, sb=A, off=A, E=2, M=10, d=A, dt=0, N=128, K=
     (lambda: gemm(ldsb=1 << 22), fp8bs.ERR_UNSUPPORTED_SHAPE),
     (lambda: gemm(M=0), fp8bs.OK),
     (lambda: gemm(N=0), fp8bs.OK),
+    (lambda: swiglu(I=200, ldg=256, ldu=256, ldq=256, ldh=256), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: swiglu(T=-1), fp8bs.ERR_INVALID_ARG),
+    (lambda: swiglu(I=0), fp8bs.ERR_INVALID_ARG),
+    (lambda: swiglu(g=NULL), fp8bs.ERR_INVALID_ARG),
+    (lambda: swiglu(q=NULL), fp8bs.ERR_INVALID_ARG),                  # codes without scales
+    (lambda: swiglu(q=NULL, s=NULL, h=NULL), fp8bs.ERR_INVALID_ARG),  # no output
+    (lambda: swiglu(ldu=128), fp8bs.ERR_INVALID_ARG),
+    (lambda: swiglu(lds=1), fp8bs.ERR_INVALID_ARG),
+    (lambda: swiglu(u=A + 8), fp8bs.ERR_MISALIGNED),
+    (lambda: swiglu(ldh=260), fp8bs.ERR_MISALIGNED),
+    (lambda: swiglu(T=0), fp8bs.OK),
     (lambda: gemm_bf16a(dt=5), fp8bs.ERR_INVALID_ARG),
     (lambda: gemm_bf16a(K=192, ldx=256, ldb=256, ldqx=256), fp8bs.ERR_UNSUPPORTED_SHAPE),
     (lambda: gemm_bf16a(M=-1), fp8bs.ERR_INVALID_ARG),
@@ -346,6 +361,23 @@ def test_binding_refuses_mismatched_bf16a_operands():
         fp8bs.fp8bs_gemm_bf16a(x, qx, sx, b, sb, d, fp8bs.OUT_F32, stream=0)
     with pytest.raises(ValueError, match="dimension 1"):
         fp8bs.fp8bs_gemm_bf16a(x, qx, sx, b, sb, d[:, :299], fp8bs.OUT_BF16, stream=0)
+
+
+def test_binding_refuses_mismatched_swiglu_operands():
+    import torch
+    g = torch.zeros((10, 256), dtype=torch.bfloat16)
+    q = torch.zeros((10, 256), dtype=torch.uint8)
+    s = torch.zeros((10, 2), dtype=torch.float32)
+    with pytest.raises(ValueError, match="dimension 0"):
+        fp8bs.fp8bs_swiglu_quant_1x128(g, g[:9], q, s, None, stream=0)
+    with pytest.raises(ValueError, match="both or neither"):
+        fp8bs.fp8bs_swiglu_quant_1x128(g, g, q, None, None, stream=0)
+    with pytest.raises(ValueError, match="no output"):
+        fp8bs.fp8bs_swiglu_quant_1x128(g, g, None, None, None, stream=0)
+    with pytest.raises(ValueError, match="dimension 1"):
+        fp8bs.fp8bs_swiglu_quant_1x128(g, g, q, s[:, :1], None, stream=0)
+    with pytest.raises(ValueError, match="dtype"):
+        fp8bs.fp8bs_swiglu_quant_1x128(g, g, q, s, g.float(), stream=0)
 
 
 def test_binding_refuses_host_tensors():
