@@ -35,8 +35,11 @@ namespace {
 // reduction over the 8 lanes that share the channel (DPP), each thread
 // derives the scales of only its own CPT channels, and each channel's 16
 // codes leave as one 16-byte store.
+// Four 256-thread workgroups per compute unit (the launch's grid assumes
+// them): 4 waves per SIMD, so at most 128 VGPRs per wave.  (Left to itself
+// the FP8-source kernel took 130, which let only three workgroups in.)
 template <bool SRC_BF16>
-__global__ __launch_bounds__(256) void requant_kernel(const uint8_t* __restrict__ in,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void requant_kernel(const uint8_t* __restrict__ in,
                                                       const float* __restrict__ s_in, int64_t T,
                                                       int64_t ld_in_bytes, int64_t lds_in,
                                                       uint8_t* __restrict__ q_out, int64_t ld_out,
@@ -178,7 +181,7 @@ __device__ __forceinline__ void transpose4x4(const uint32_t (&w)[4], uint32_t (&
   t[3] = __builtin_amdgcn_perm(y1, x1, 0x07060302u);
 }
 
-__global__ __launch_bounds__(256) void transpose_w_kernel(const uint8_t* __restrict__ q, int64_t ldq,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void transpose_w_kernel(const uint8_t* __restrict__ q, int64_t ldq,
                                                           const float* __restrict__ s, int64_t lds,
                                                           uint8_t* __restrict__ qt, int64_t ldqt,
                                                           float* __restrict__ st, int64_t ldst,
