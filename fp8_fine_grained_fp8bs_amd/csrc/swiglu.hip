@@ -14,11 +14,12 @@
 //
 // h is computed in FP32: sigma(g) from e = exp(-|g|) (never overflows):
 // 1 / (1 + e) for g >= 0, e / (1 + e) for g < 0; h = (g sigma) u, within a
-// few units in the last place of the exact value.  The codes and scales are
-// those of the FP32 tile quantizer (s = fl32(amax / 448) by IEEE division,
-// the exact two-bracket encoding) applied to these FP32 values.  A 16-lane
-// DPP row takes one tile, 8 values per lane; each row keeps four tiles of
-// loads in flight.
+// few units in the last place of the exact value.
+// The codes and scales are those of the FP32 tile quantizer (s = fl32(amax
+// / 448) by IEEE division, the exact two-bracket encoding) applied to these
+// FP32 values.  A 16-lane DPP row takes one tile, 8 values per lane; each
+// row keeps two tiles of loads in flight (measured faster than one, four or
+// eight tiles: fewer registers, more resident waves).
 #include <hip/hip_runtime.h>
 
 #include "fp8bs_device.h"
@@ -27,7 +28,7 @@
 namespace fp8bs {
 namespace {
 
-constexpr int kTilesPerRow = 4;   // tiles of one DPP row, loaded before any is encoded
+constexpr int kTilesPerRow = 2;   // tiles of one DPP row, loaded before any is encoded
 
 // e^-a for a >= 0 by the hardware's 2^x (v_exp_f32, within about one unit
 // in the last place) after the argument reduction of Cody and Waite
