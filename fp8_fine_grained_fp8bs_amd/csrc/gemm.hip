@@ -93,7 +93,9 @@ struct Cfg {
   static constexpr int slot_bytes(bool brow) { return SA_BYTES + sb_bytes(brow); }
   static constexpr int sc_area() { return NSTAGE * STAGE; }
   static constexpr int dummy_off(bool brow) { return sc_area() + NSLOT * slot_bytes(brow); }
-  static constexpr int lds_bytes(bool brow) { return dummy_off(brow) + 256; }
+  // the next tile's four buffer descriptors (A, B, A scales, B scales)
+  static constexpr int next_off(bool brow) { return dummy_off(brow) + 256; }
+  static constexpr int lds_bytes(bool brow) { return next_off(brow) + 64; }
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
   static_assert((BM + BN) % (8 * NW) == 0, "tile copies must split evenly over the waves");
   static_assert(BM % 64 == 0 && BN % 64 == 0, "scale copies move 16-row units, SBLK per lane row");
@@ -315,17 +317,20 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
 
   // ---- tiles: the workgroup walks the virtual workgroup ids blockIdx.x,
   //      blockIdx.x + gridDim.x, ... (gridDim.x is a multiple of the XCD
-  //      count, so every tile of a workgroup maps to the same XCD); the
-  //      first K groups of the next tile are copied while the current tile's
-  //      results are written out.
+  //      count, so every tile of a workgroup maps to the same XCD).
+  //      plan_tile(v, ...) gives virtual tile v's first row, row end, first
+  //      column and its expert's B and B scales (false: no such tile).
   int64_t m0 = 0, m_end = 0, n0 = 0;
   const uint8_t* bmat = p.b;
   const float* sbmat = p.sb;
   const int vtiles = p.tiles_m * p.tiles_n;
-  auto plan_tile = [&](int v) -> bool {
+  auto plan_tile = [&](int v, int64_t& m0, int64_t& m_end, int64_t& n0, const uint8_t*& bmat,
+                       const float*& sbmat) -> bool {
     int vm, nt;
     tile_of<GROUPED ? GROUP_M_EXPERTS : GROUP_M>(v, p.tiles_m, p.tiles_n, vm, nt);
     n0 = static_cast<int64_t>(nt) * BN;
+    bmat = p.b;
+    sbmat = p.sb;
     if (GROUPED) {
       int64_t mt = vm;
       for (int e = 0; e < p.E; ++e) {
@@ -427,27 +432,45 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
       }
     }
   }
-  // per-tile descriptors
-  auto set_descriptors = [&]() {
+  // per-tile descriptors: A and B rows, A scales, B scales
+  struct TileDesc {
+    i32x4 a, b, sa, sb;
+  };
+  auto descriptors = [&](int64_t m0, int64_t m_end, int64_t n0, const uint8_t* bmat,
+                         const float* sbmat) -> TileDesc {
     const int64_t rows_a = m_end - m0 < BM ? m_end - m0 : BM;
     const int64_t rows_b = p.N - n0 < BN ? p.N - n0 : BN;
-    rs_a = make_rsrc(p.a + m0 * p.lda, static_cast<uint32_t>(rows_a * p.lda));
-    rs_b = make_rsrc(bmat + n0 * p.ldb, static_cast<uint32_t>(rows_b * p.ldb));
-    const i32x4 rs_sa = make_rsrc(p.sa + m0 * p.ldsa, static_cast<uint32_t>(rows_a) * ldsa4);
-#pragma unroll
-    for (int u = 0; u < SPW; ++u) {
-      const int c = wave + u * C::NW;
-      if (c >= SAW && c < SAW + SBW) {
-        if (BROW) {
-          sc[u].rs = make_rsrc(sbmat + n0 * p.ldsb, static_cast<uint32_t>(rows_b) * ldsb4);
-        } else {
-          const int64_t blocks = (rows_b + 127) / 128;
-          sc[u].rs = make_rsrc(sbmat + (n0 / 128) * p.ldsb, static_cast<uint32_t>(blocks) * ldsb4);
-        }
-      } else {
-        sc[u].rs = rs_sa;
-      }
+    TileDesc d;
+    d.a = make_rsrc(p.a + m0 * p.lda, static_cast<uint32_t>(rows_a * p.lda));
+    d.b = make_rsrc(bmat + n0 * p.ldb, static_cast<uint32_t>(rows_b * p.ldb));
+    d.sa = make_rsrc(p.sa + m0 * p.ldsa, static_cast<uint32_t>(rows_a) * ldsa4);
+    if (BROW) {
+      d.sb = make_rsrc(sbmat + n0 * p.ldsb, static_cast<uint32_t>(rows_b) * ldsb4);
+    } else {
+      const int64_t blocks = (rows_b + 127) / 128;
+      d.sb = make_rsrc(sbmat + (n0 / 128) * p.ldsb, static_cast<uint32_t>(blocks) * ldsb4);
     }
+    return d;
+  };
+  // whether this wave's scale copy u moves B scales (else A scales, or a
+  // dummy copy of A scales)
+  auto copies_sb = [&](int u) {
+    const int c = wave + u * C::NW;
+    return c >= SAW && c < SAW + SBW;
+  };
+  auto set_tile_copies = [&](const TileDesc& d) {
+    rs_a = d.a;
+    rs_b = d.b;
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) sc[u].rs = copies_sb(u) ? d.sb : d.sa;
+  };
+  // descriptor k of the next tile's record in LDS, made uniform
+  auto next_desc = [&](int k) -> i32x4 {
+    const i32x4 d = *reinterpret_cast<const i32x4*>(lds + C::next_off(BROW) + 16 * k);
+    i32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = __builtin_amdgcn_readfirstlane(d[e]);
+    return r;
   };
 
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&lds[0]));
@@ -507,80 +530,139 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     return reinterpret_cast<const float*>(lds + C::sc_area() + ((g / SBLK) % NSLOT) * SLOT);
   };
 
+  // Tile stream.  When G is a multiple of SBLK and at least 8, tile
+  // boundaries fall on scale-block boundaries, and a tile's last issues copy
+  // its successor's first scale block (issues G - 4 .. G - 1) and first
+  // three K groups (issues G .. G + 2); its last iteration reads the
+  // successor's first fragments.  The successor then starts with no head
+  // copies and no wait: only the output tile goes through LDS in between.
+  // Stages, scale slots and fragment sets then follow the workgroup's
+  // running group count u (tile k's group g has u = k G + g): stage u % 3,
+  // slot (u / 4) % 3, set u % 2.  j0 = (k G) % 12 (0, 4 or 8) is the
+  // phase of a tile's group 0 in that period-12 pattern; the unrolled loop
+  // runs rounds of 12 values of u, so every index stays a constant.  At the
+  // two switch points the copies take the successor's descriptors, which
+  // the tile start leaves in LDS.  Otherwise (and for a workgroup's first
+  // tile) the head copies are issued after the last group, j0 = 0.
+  const bool streamable = G % SBLK == 0 && G >= 8;
+  const int nblk = G / SBLK;  // scale blocks per tile (when streamable)
+
   int v = blockIdx.x;
-  while (v < vtiles && !plan_tile(v)) v += gridDim.x;
+  while (v < vtiles && !plan_tile(v, m0, m_end, n0, bmat, sbmat)) v += gridDim.x;
   if (v >= vtiles) return;  // uniform per workgroup
-  set_descriptors();
+  set_tile_copies(descriptors(m0, m_end, n0, bmat, sbmat));
   issue_head();
 
+  bool head = true;
+  int j0 = 0;
+  Frag<C> f0, f1;
   for (;;) {
+    // ---- the workgroup's next tile; its descriptors go to LDS for the
+    //      switch points (read there after at least one barrier)
+    int vn = v + gridDim.x;
+    {
+      int64_t nm0, nm_end, nn0;
+      const uint8_t* nb;
+      const float* nsb;
+      while (vn < vtiles && !plan_tile(vn, nm0, nm_end, nn0, nb, nsb)) vn += gridDim.x;
+      if (streamable && vn < vtiles && tid == 0) {
+        const TileDesc d = descriptors(nm0, nm_end, nn0, nb, nsb);
+        i32x4* rec = reinterpret_cast<i32x4*>(lds + C::next_off(BROW));
+        rec[0] = d.a;
+        rec[1] = d.b;
+        rec[2] = d.sa;
+        rec[3] = d.sb;
+      }
+    }
+    const bool more = vn < vtiles;
+    const bool pre = streamable && more;  // this tile prefetches the next one
+
     v4f acc[C::MB][C::NB];
 #pragma unroll
     for (int i = 0; i < C::MB; ++i)
 #pragma unroll
       for (int j = 0; j < C::NB; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Pipeline over three stages, stage(x) = x % 3.  Before iteration g:
-    // fragments of group g are in registers (cur), stage(g + 1) holds group
-    // g + 1 and is visible, the copy of group g + 2 into stage(g + 2) is in
-    // flight.  Iteration g reads the fragments of g + 1, starts issue g + 3
-    // into stage(g) (whose reads finished before the last barrier),
-    // multiplies g, then waits for issue g + 2 and for its own LDS reads
-    // before the barrier.  Scale block h is copied by issues 4h - 4 ..
-    // 4h - 1 (iterations 4h - 7 .. 4h - 4), is first read in iteration
-    // 4h - 1, and its slot (NSLOT = 3) was last read in iteration
-    // 4h - 10.  Copies and reads past the last group are clamped to valid
-    // data that is never used.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this tile's head copies (and earlier stores)
-    block_barrier();
-    Frag<C> f0, f1;
-    load_frag<C, BROW>(f0, lds, slot_of(0), 0, wm, wn, lane);
-    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
-    issue(2, 2);
-    block_barrier();
+    // Pipeline over three stages.  Before iteration g: fragments of group
+    // g are in registers (cur), the stage of group g + 1 holds it and is
+    // visible, the copy of group g + 2 is in flight.  Iteration g reads the
+    // fragments of g + 1, starts issue g + 3 into the stage of group g
+    // (whose reads finished before the last barrier), multiplies g, then
+    // waits for issue g + 2 and for its own LDS reads before the barrier.
+    // Scale block h is copied by issues 4h - 4 .. 4h - 1 (iterations
+    // 4h - 7 .. 4h - 4), is first read in iteration 4h - 1, and its slot
+    // (NSLOT = 3) was last read in iteration 4h - 10.  Without a successor
+    // to prefetch, copies and reads past the last group are clamped to
+    // valid data that is never used.
+    if (head) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this tile's head copies (and earlier stores)
+      block_barrier();
+      load_frag<C, BROW>(f0, lds, slot_of(0), 0, wm, wn, lane);
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+      issue(2, 2);
+      block_barrier();
+    }
 
     // Unrolled by 12 (fragment sets alternate with period 2, stages with 3,
     // scale quarters with 4, scale slots with 12) so that every stage, slot
     // and quarter index is a constant; iteration g + i runs only if
-    // g + i < G.  The last iteration reads fragments of the (clamped)
-    // group G, which are never used.
-    for (int g = 0; g < G; g += 12) {
-      const int hb = g / 4;  // scale blocks before this round
+    // 0 <= g + i < G.  Issues past the last group copy from the successor
+    // once the switch points have passed (gsub, hsub: its group and block
+    // numbers are those of this tile minus G and nblk).
+    int gsub = 0, hsub = 0;
+    for (int g = -j0; g < G; g += 12) {
+      const int hb = g / 4;  // scale blocks before this round (g is a multiple of 4)
 #pragma unroll
       for (int i = 0; i < 12; ++i) {
-        if (g + i < G) {
+        if (static_cast<unsigned>(g + i) < static_cast<unsigned>(G)) {
           Frag<C>& cur = (i & 1) ? f1 : f0;
           Frag<C>& nxt = (i & 1) ? f0 : f1;
           const int t = g + i + 3;                   // this iteration's issue
           const int q = (i + 3) & 3;                 // its scale quarter
           const int hl = (i + 3) / 4 + 1;            // its scale block, minus hb
+          // G + j0 is a multiple of 4, so both switch points (issues G - 4
+          // and G, iterations G - 7 and G - 3) fall where i % 4 == 1
+          if ((i & 3) == 1 && pre) {
+            if (t == G - 4) {
+#pragma unroll
+              for (int u = 0; u < SPW; ++u) sc[u].rs = next_desc(copies_sb(u) ? 3 : 2);
+              hsub = nblk;
+            } else if (t == G) {
+              rs_a = next_desc(0);
+              rs_b = next_desc(1);
+              gsub = G;
+            }
+          }
           const float* slot_n = reinterpret_cast<const float*>(
-              lds + C::sc_area() + (((i + 1) / 4) % NSLOT) * SLOT);  // group g + i + 1 (hb % 3 == 0)
+              lds + C::sc_area() + (((i + 1) / 4) % NSLOT) * SLOT);  // group g + i + 1
           pipelined_group<C, BROW, COPIES>(
               acc, cur, nxt, lds + ((i + 1) % 3) * C::STAGE, slot_n, (i + 1) & 3, wm, wn, lane,
-              [&](int k) { issue_part_q(t, i % 3, q, hb + hl, hl % NSLOT, k); });
+              [&](int k) { issue_part_q(t - gsub, i % 3, q, hb + hl - hsub, hl % NSLOT, k); });
           __builtin_amdgcn_s_waitcnt(waitcnt_vm(COPIES));
           __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
           block_barrier();
         }
       }
     }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the clamped copies past the last group
-    block_barrier();                            // every stage and scale slot is free
 
-    // ---- next tile: its head copies go out before this tile's results
+    // ---- the next tile becomes current; without the stream its head
+    //      copies go out before this tile's results
     const int64_t cm0 = m0, cm_end = m_end, cn0 = n0;
-    v += gridDim.x;
-    while (v < vtiles && !plan_tile(v)) v += gridDim.x;
-    const bool more = v < vtiles;
-    if (more) {
-      set_descriptors();
-      issue_head();
+    if (more) plan_tile(vn, m0, m_end, n0, bmat, sbmat);
+    if (!pre) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the clamped copies past the last group
+      block_barrier();                            // every stage and scale slot is free
+      if (more) {
+        set_tile_copies(descriptors(m0, m_end, n0, bmat, sbmat));
+        issue_head();
+      }
     }
 
-    // ---- epilogue through stage 2 of the LDS (padded rows, PR rows per
-    //      pass), so that every global store writes 16 contiguous bytes per
-    //      lane and a wave writes whole output rows.  Lane (fr, kc) holds
+    // ---- epilogue through a free stage of the LDS (the stage of the next
+    //      tile's group 0, read out in the last iteration, or stage 2 after
+    //      head copies into stages 0 and 1), padded rows, PR rows per pass,
+    //      so that every global store writes 16 contiguous bytes per lane
+    //      and a wave writes whole output rows.  Lane (fr, kc) holds
     //      columns 4 kc .. 4 kc + 3 of row fr of each 16x16 block.  The
     //      stores carry the non-temporal hint: the kernel never reads its
     //      output, and the caches stay with the operand panels.
@@ -590,7 +672,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     constexpr int PR0 = C::STAGE / ROWB;          // rows that fit one stage
     constexpr int PR = PR0 >= BM ? BM : PR0 >= 128 ? 128 : PR0 >= 64 ? 64 : PR0 >= 32 ? 32 : 16;
     static_assert(PR <= PR0 && BM % PR == 0, "output passes");
-    uint8_t* const ob = lds + 2 * C::STAGE;
+    uint8_t* const ob = lds + (pre ? (j0 + G) % 3 : 2) * C::STAGE;
     uint8_t* dbase = static_cast<uint8_t*>(p.d);
     const int64_t ldd_b = p.ldd * OB;
     const int64_t cols = p.N - cn0 < BN ? p.N - cn0 : BN;   // valid columns of the tile
@@ -671,6 +753,10 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
       }
     }
     if (!more) break;
+    if (pre) block_barrier();  // the staged output is read out before its stage takes group 3
+    v = vn;
+    head = !pre;
+    j0 = pre ? (j0 + G) % 12 : 0;
   }
 }
 
