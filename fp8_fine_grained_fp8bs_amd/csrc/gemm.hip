@@ -555,8 +555,12 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
 
   bool head = true;
   int j0 = 0;
-  Frag<C> f0, f1;
+  // Fragment set f0 carries the next tile's group 0 across the epilogue.
+  // Every tile starts at an even position (j0 is 0, 4 or 8), which reads f0
+  // and fills f1, so f1 starts each tile unset and holds nothing across.
+  Frag<C> f0;
   for (;;) {
+    Frag<C> f1;
     // ---- the workgroup's next tile; its descriptors go to LDS for the
     //      switch points (read there after at least one barrier)
     int vn = v + gridDim.x;
