@@ -680,12 +680,21 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     uint8_t* dbase = static_cast<uint8_t*>(p.d);
     const int64_t ldd_b = p.ldd * OB;
     const int64_t cols = p.N - cn0 < BN ? p.N - cn0 : BN;   // valid columns of the tile
+    // a whole tile whose pass fits 32-bit lane offsets (uniform)
+    const bool full = cols == BN && cm_end - cm0 >= BM && ldd_b * PR < (int64_t(1) << 31);
+    // The thread index passes through an empty asm statement, so the lane
+    // addresses below are computed here for each tile: hoisted out of the
+    // tile loop they would be spilled, and each reload from scratch waits
+    // for every copy and store in flight.
+    int et = tid;
+    asm volatile("" : "+v"(et));
+    const int elane = et & 63;
 #pragma unroll
     for (int pass = 0; pass < BM / PR; ++pass) {
       if (pass > 0) block_barrier();  // previous pass read out of the LDS
       {
-        const int fr = lane & 15;
-        const int kc = lane >> 4;
+        const int fr = elane & 15;
+        const int kc = elane >> 4;
 #pragma unroll
         for (int i = 0; i < C::MB; ++i) {
           const int rb = wm * (C::MB * 16) + i * 16;  // first row of the block
@@ -738,9 +747,21 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
             if (sub == 0) p.s_out[m * p.lds_out + (cn0 + c0) / 128] = ts.s;
           }
         }
+      } else if (full) {
+        // a whole tile: no bounds, one base address per pass
+        static_assert((PR * CPR) % C::NT == 0, "whole store rounds");
+        uint8_t* const tb = dbase + (cm0 + pass * PR) * ldd_b + cn0 * OB;
+#pragma unroll
+        for (int k = 0; k < PR * CPR / C::NT; ++k) {
+          const int ch = et + k * C::NT;
+          const int r = ch / CPR, cc = ch % CPR;
+          const uint4 vv = *reinterpret_cast<const uint4*>(ob + r * ROWB + cc * 16);
+          const uint32_t off = static_cast<uint32_t>(r) * static_cast<uint32_t>(ldd_b) + cc * 16;
+          __builtin_nontemporal_store(u32x4{vv.x, vv.y, vv.z, vv.w}, reinterpret_cast<u32x4*>(tb + off));
+        }
       } else {
   #pragma unroll 4
-        for (int ch = tid; ch < PR * CPR; ch += C::NT) {
+        for (int ch = et; ch < PR * CPR; ch += C::NT) {
           const int r = ch / CPR, cc = ch % CPR;
           const int64_t m = cm0 + pass * PR + r;
           const int c0 = cc * (16 / OB);
@@ -750,8 +771,12 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
           if (c0 + 16 / OB <= cols) {
             __builtin_nontemporal_store(u32x4{vv.x, vv.y, vv.z, vv.w}, reinterpret_cast<u32x4*>(dst));
           } else {
-            const uint8_t* src = reinterpret_cast<const uint8_t*>(&vv);
-            for (int e = 0; e < (cols - c0) * OB; ++e) dst[e] = src[e];
+            // the row's last columns: byte by byte from the chunk's words
+            const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+            const int nb = static_cast<int>(cols - c0) * OB;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              if (e < nb) dst[e] = static_cast<uint8_t>(w[e >> 2] >> (8 * (e & 3)));
           }
         }
       }
