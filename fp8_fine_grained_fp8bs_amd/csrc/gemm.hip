@@ -543,8 +543,12 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   // runs rounds of 12 values of u, so every index stays a constant.  At the
   // two switch points the copies take the successor's descriptors, which
   // the tile start leaves in LDS.  Otherwise (and for a workgroup's first
-  // tile) the head copies are issued after the last group, j0 = 0.
-  const bool streamable = G % SBLK == 0 && G >= 8;
+  // tile) the head copies are issued after the last group, j0 = 0.  The
+  // quantized output keeps the head: its epilogue (FP32 staging and the
+  // encoder) with a fragment set held across it spills, and measured
+  // slower than without the stream (544 against 517 us at 4096 x 18432 x
+  // 7168).
+  const bool streamable = OUT != kOutFp8 && G % SBLK == 0 && G >= 8;
   const int nblk = G / SBLK;  // scale blocks per tile (when streamable)
 
   int v = blockIdx.x;

@@ -8,9 +8,10 @@ With at most 256 tiles every workgroup runs one tile and no stream is
 involved; each output element goes through the same operations in the
 same order either way.  So the output of a launch with several tiles per
 workgroup must equal, bit for bit, the outputs of launches over row slices
-of at most 256 tiles each, in every output form, both B-scale modes and the
-grouped form, at G values that give every phase; the full outputs are also
-checked against the oracle on sampled entries.
+of at most 256 tiles each: BF16 and FP32 outputs, both B-scale modes and
+the grouped form, at G values that give every phase, and the quantized
+output (which does not stream); the full outputs are also checked against
+the oracle on sampled entries.
 """
 import numpy as np
 import pytest
@@ -101,7 +102,9 @@ def test_stream_row_scales_f32(G):
 
 @pytest.mark.parametrize("G", [8, 16])
 def test_stream_quantized_output(G):
-    """Output quantized 1x128 in the epilogue: codes and scales."""
+    """Output quantized 1x128 in the epilogue: codes and scales.  This form
+    keeps the head copies on every tile (no stream); several tiles per
+    workgroup must still match single-tile launches."""
     native_loaded()
     M, N, K = 128 * 40 - 3, 256 * 20, 128 * G
     qa, sa, qb, sb = _operands(M, N, K, seed=200 + G)
