@@ -164,6 +164,14 @@ __device__ __forceinline__ void gemm_copy4(const i32x4& rsrc, uint32_t voff, uin
                :: "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
 
+// This lane's index in its wave, computed by the asm statement itself where
+// it stands (it can be neither hoisted nor kept across the code around it).
+__device__ __forceinline__ int opaque_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // Fragments (and their scales) of one K group for one wave.
 template <class C>
 struct Frag {
@@ -396,34 +404,42 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   };
   ScaleCopy sc[SPW];
   const uint32_t ldsa4 = static_cast<uint32_t>(p.ldsa * 4), ldsb4 = static_cast<uint32_t>(p.ldsb * 4);
+  // VGPR offset of this wave's scale copy u for lane index ln
+  auto scale_voff = [&](int u, int ln) -> uint32_t {
+    const int c = wave + u * C::NW;
+    const uint32_t gl = static_cast<uint32_t>(ln >> 4) * 4u;
+    if (c < SAW) return static_cast<uint32_t>(16 * c + (ln & 15)) * ldsa4 + gl;
+    if (c < SAW + SBW) {
+      const int w = c - SAW;
+      return BROW ? static_cast<uint32_t>(16 * w + (ln & 15)) * ldsb4 + gl
+                  : static_cast<uint32_t>(ln & 15) * ldsb4 + gl;
+    }
+    return 0;
+  };
   {
-    const uint32_t gl = static_cast<uint32_t>(lane >> 4) * 4u;
 #pragma unroll
     for (int u = 0; u < SPW; ++u) {
       const int c = wave + u * C::NW;
       ScaleCopy& x = sc[u];
       x.hstep = SBLK * 4;
       x.slot = C::slot_bytes(BROW);
+      x.voff = scale_voff(u, lane);
       if (c < SAW) {
-        x.voff = static_cast<uint32_t>(16 * c + (lane & 15)) * ldsa4 + gl;
         x.qstep = 16 * SAW * ldsa4;
         x.dst0 = c * 256;
         x.dstq = SAW * 256;
       } else if (c < SAW + SBW) {
         const int w = c - SAW;
         if (BROW) {
-          x.voff = static_cast<uint32_t>(16 * w + (lane & 15)) * ldsb4 + gl;
           x.qstep = 16 * SBW * ldsb4;
           x.dst0 = C::SA_BYTES + w * 256;
           x.dstq = SBW * 256;
         } else {
-          x.voff = static_cast<uint32_t>(lane & 15) * ldsb4 + gl;
           x.qstep = 0;
           x.dst0 = C::SA_BYTES;
           x.dstq = 0;
         }
       } else {
-        x.voff = 0;
         x.qstep = 0;
         x.hstep = 0;
         x.dst0 = C::dummy_off(BROW) - C::sc_area();
@@ -482,11 +498,12 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   // quarter's row offset and the block's group offset are added to the
   // VGPR offset, so the descriptor's range check covers the whole address
   // (the SGPR offset stays zero).
-  auto issue_scales = [&](int u, int q, int h, int hs) {
+  auto issue_scales_v = [&](int u, uint32_t voff, int q, int h, int hs) {
     const ScaleCopy& x = sc[u];
     const uint32_t dst = lds_base + C::sc_area() + hs * x.slot + x.dst0 + x.dstq * q;
-    gemm_copy4(x.rs, x.voff + x.qstep * q + x.hstep * h, 0, dst);
+    gemm_copy4(x.rs, voff + x.qstep * q + x.hstep * h, 0, dst);
   };
+  auto issue_scales = [&](int u, int q, int h, int hs) { issue_scales_v(u, sc[u].voff, q, h, hs); };
   // part k of issue t: tile copy k (k < DPW) of K group min(t, G - 1) into
   // `stage`, or (k >= DPW) copy k - DPW of quarter t % 4 of scale block
   // t / 4 + 1 (block 0 is copied with the first two issues)
@@ -518,13 +535,24 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
   };
   // the copies a tile needs before its first barrier: scale block 0 and
   // issues 0 and 1
+  // (with scale offsets made here: kept from the set-up they are spilled
+  // around the epilogue, and each reload would wait for the copies before)
   auto issue_head = [&]() {
+    const int hl = opaque_lane();
+    uint32_t vb[SPW];
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) vb[u] = scale_voff(u, hl);
 #pragma unroll
     for (int q = 0; q < SBLK; ++q)
 #pragma unroll
-      for (int u = 0; u < SPW; ++u) issue_scales(u, q, 0, 0);
-    issue(0, 0);
-    issue(1, 1);
+      for (int u = 0; u < SPW; ++u) issue_scales_v(u, vb[u], q, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int k = 0; k < COPIES; ++k) {
+        if (k < C::DPW) issue_part(t, t, k);
+        else issue_scales_v(k - C::DPW, vb[k - C::DPW], t & 3, 1, 1 % NSLOT);
+      }
   };
   auto slot_of = [&](int g) {
     return reinterpret_cast<const float*>(lds + C::sc_area() + ((g / SBLK) % NSLOT) * SLOT);
@@ -605,7 +633,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     if (head) {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this tile's head copies (and earlier stores)
       block_barrier();
-      load_frag<C, BROW>(f0, lds, slot_of(0), 0, wm, wn, lane);
+      load_frag<C, BROW>(f0, lds, slot_of(0), 0, wm, wn, opaque_lane());  // addresses made here, not reloaded
       __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
       issue(2, 2);
       block_barrier();
@@ -686,17 +714,15 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
     const int64_t cols = p.N - cn0 < BN ? p.N - cn0 : BN;   // valid columns of the tile
     // a whole tile whose pass fits 32-bit lane offsets (uniform)
     const bool full = cols == BN && cm_end - cm0 >= BM && ldd_b * PR < (int64_t(1) << 31);
-    // The thread index passes through an empty asm statement, so the lane
-    // addresses below are computed here for each tile: hoisted out of the
-    // tile loop they would be spilled, and each reload from scratch waits
+    // The lane addresses below come from a lane index made where each part
+    // uses it (opaque_lane): hoisted out of the tile loop, or carried across
+    // the passes, they would be spilled, and each reload from scratch waits
     // for every copy and store in flight.
-    int et = tid;
-    asm volatile("" : "+v"(et));
-    const int elane = et & 63;
 #pragma unroll
     for (int pass = 0; pass < BM / PR; ++pass) {
       if (pass > 0) block_barrier();  // previous pass read out of the LDS
       {
+        const int elane = opaque_lane();
         const int fr = elane & 15;
         const int kc = elane >> 4;
 #pragma unroll
@@ -755,6 +781,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
         // a whole tile: no bounds, one base address per pass
         static_assert((PR * CPR) % C::NT == 0, "whole store rounds");
         uint8_t* const tb = dbase + (cm0 + pass * PR) * ldd_b + cn0 * OB;
+        const int et = wave * 64 + opaque_lane();
 #pragma unroll
         for (int k = 0; k < PR * CPR / C::NT; ++k) {
           const int ch = et + k * C::NT;
@@ -764,6 +791,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
           __builtin_nontemporal_store(u32x4{vv.x, vv.y, vv.z, vv.w}, reinterpret_cast<u32x4*>(tb + off));
         }
       } else {
+        const int et = wave * 64 + opaque_lane();
   #pragma unroll 4
         for (int ch = et; ch < PR * CPR; ch += C::NT) {
           const int r = ch / CPR, cc = ch % CPR;

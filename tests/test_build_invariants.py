@@ -8,7 +8,7 @@ assembly and reads it).
   `v_pk_add_f32`): the build disables it, and the kernels' FP32 arithmetic
   is written as scalar operations.
 * Kernels whose grid assumes a number of resident waves fit the registers
-  of that occupancy, and no kernel but the block-scaled GEMM spills.
+  of that occupancy, and no kernel spills to scratch.
 """
 import functools
 import os
@@ -84,9 +84,11 @@ def test_register_budget_of_the_launch(src, frag, waves):
         assert 512 // alloc >= waves, f"{name}: {vgpr} VGPRs allow {512 // alloc} waves per SIMD, launch assumes {waves}"
 
 
-@pytest.mark.parametrize("src", [s for s in build.SOURCES if s not in ("api.hip", "gemm.hip")])
+@pytest.mark.parametrize("src", [s for s in build.SOURCES if s != "api.hip"])
 def test_no_register_spills(src):
-    """No kernel spills to scratch (the block-scaled GEMM keeps a few
-    addresses outside its K loop in scratch, and is left out)."""
+    """No kernel spills to scratch.  In the persistent GEMM a reload from
+    scratch waits for every copy and store in flight (a scratch load counts
+    in the same vector-memory counter), so a spilled address costs a full
+    memory round trip wherever it is reloaded."""
     for name, (_, priv) in _kernels(src).items():
         assert priv == 0, f"{name}: {priv} bytes of scratch"
