@@ -143,3 +143,23 @@ def test_stream_grouped(G):
     got = host(full)[mi, ni].astype(np.float64)
     mag = oracle.grouped_gemm_entries(qa & 0x7F, np.abs(sa), qb & 0x7F, np.abs(sb), off, mi, ni)
     assert (np.abs(got - ref) <= 1e-3 * mag).all(), f"grouped G={G}: sampled entries off the oracle"
+
+
+@pytest.mark.parametrize("M", [1, 3, 129])
+def test_stream_thin_m(M):
+    """A few rows and more than 256 column tiles: workgroups stream from
+    one ragged single-M-tile tile to the next along N."""
+    native_loaded()
+    N, K = 256 * 300 - 40, 128 * 12
+    qa, sa, qb, sb = _operands(M, N, K, seed=400 + M)
+    announce(f"stream thin M={M} N={N} K={K}")
+    a, sa_d, b, sb_d = _dev(qa), _dev(sa), _dev(qb), _dev(sb)
+    full = fp8bs.gemm(a, sa_d, b, sb_d, fp8bs.BSCALE_BLOCK_128x128, out_f32=True)
+    # column slices of at most 256 tiles (128 column tiles x at most 2 row
+    # tiles): the same operations on every element
+    for n0 in range(0, N, 256 * 128):
+        n1 = min(N, n0 + 256 * 128)
+        part = fp8bs.gemm(a, sa_d, b[n0:n1], sb_d[n0 // 128:-(-n1 // 128)], fp8bs.BSCALE_BLOCK_128x128, out_f32=True)
+        fb, pb = _bits(full[:, n0:n1]), _bits(part)
+        assert (fb == pb).all(), f"thin M={M}: columns {n0}..{n1}: {(fb != pb).sum()} entries differ"
+    sampled_check(f"stream thin M={M}", qa, sa, qb, sb, full)
