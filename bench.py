@@ -10,8 +10,10 @@ The inputs (seeded synthetic bf16, the heavy-tailed recipe of
 timed region starts.  ``value`` is the step's throughput in GEMM TFLOP/s
 (2*M*N*K flop per step divided by the wall time of the step, quantization
 included).  Each kernel is also timed with HIP events on the stream it runs
-on; the GEMM is the dominant kernel and its roofline fraction is reported
-against the MI355X dense FP8 peak.
+on, one event before each kernel (the span to the next event is that
+kernel's; an event costs about 2.5 us of GPU time, so the step records one
+per kernel rather than a pair); the GEMM is the dominant kernel and its
+roofline fraction is reported against the MI355X dense FP8 peak.
 
 The other hot-path rows (the up-projection GEMM with its output quantized
 for the next layer, fused and unfused; backward 1x128 -> 128x1
@@ -101,6 +103,39 @@ class KernelTimer:
 
     def reset(self):
         self.events = {}
+
+
+class ChainTimer(KernelTimer):
+    """HIP events for a sequence of kernels run back to back on the current
+    stream: one event before each kernel, and one after the last kernel of
+    the sequence; a kernel's time is the span from its event to the next.
+    Each event costs about 2.5 us of GPU time between kernels, so the
+    step records one per kernel instead of a start and an end each."""
+
+    def __init__(self):
+        super().__init__()
+        self.marks = []
+
+    def run(self, name, fn):
+        import torch
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.marks.append((name, e))
+        fn()
+
+    def close(self):
+        """Record the closing event and turn the marks into (start, end)
+        pairs per kernel name."""
+        import torch
+        end = torch.cuda.Event(enable_timing=True)
+        end.record()
+        for (name, s), (_, e) in zip(self.marks, self.marks[1:] + [(None, end)]):
+            self.events.setdefault(name, []).append((s, e))
+        self.marks = []
+
+    def reset(self):
+        super().reset()
+        self.marks = []
 
 
 class CacheFlush:
@@ -496,7 +531,7 @@ def main():
         log(f"ran {args.profile_kernel} {args.steps} times")
         return
 
-    kt = KernelTimer()
+    kt = ChainTimer()
 
     def step():
         kt.run("quant_act_w", lambda: fp8bs.fp8bs_quant_act_w(X, qx, sx, W, qw, sw))
@@ -512,6 +547,7 @@ def main():
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
+    kt.close()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall / args.steps * 1e3
