@@ -47,11 +47,13 @@
 //   group, so the ~32 workgroups resident on one XCD (8 M-tiles x 4 N-tiles
 //   at a time: the B panel of a 128x256 tile is twice the A panel) share A
 //   and B panels in that XCD's L2.
-// * Workgroups are persistent (one per compute unit): after a tile's last
-//   K group the first K groups of the workgroup's next tile are copied while
-//   the finished tile goes out through LDS with 16-byte stores, as BF16,
-//   FP32, or E4M3 codes with one scale per 1x128 tile along N (the next
-//   layer's activation quantization fused into the epilogue).
+// * Workgroups are persistent (one per compute unit).  The finished tile
+//   goes out through LDS with 16-byte stores, as BF16, FP32, or E4M3 codes
+//   with one scale per 1x128 tile along N (the next layer's activation
+//   quantization fused into the epilogue).  With K a multiple of 512 the
+//   workgroup's next tile is copied during the current tile's last K groups
+//   (the tile stream, below); otherwise its first groups are copied after
+//   the last one.
 #include <hip/hip_runtime.h>
 
 #include "fp8bs_device.h"
