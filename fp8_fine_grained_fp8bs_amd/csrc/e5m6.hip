@@ -77,7 +77,10 @@ __global__ __launch_bounds__(256) void decode_e5m6_kernel(const uint8_t* __restr
        c += static_cast<int64_t>(gridDim.x) * 256) {
     const int64_t t = c / cpr, i = c - t * cpr;
     const uint32_t* src = reinterpret_cast<const uint32_t*>(y + t * ldy + i * 12);
-    const uint32_t d0 = src[0], d1 = src[1], d2 = src[2];
+    // read once: non-temporal (41.5 against 58.5 us at 8192 x 7168 with the
+    // caches full of dirty lines)
+    const uint32_t d0 = __builtin_nontemporal_load(src), d1 = __builtin_nontemporal_load(src + 1),
+                   d2 = __builtin_nontemporal_load(src + 2);
     const uint32_t code[8] = {d0 & 0xfffu,
                               (d0 >> 12) & 0xfffu,
                               (d0 >> 24) | ((d1 & 0xfu) << 8),
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(256) void decode_e5m6_kernel(const uint8_t* __restr
 
 int64_t stream_blocks(int64_t chunks) {
   int64_t blocks = (chunks + 255) / 256;
-  return blocks > 4096 ? 4096 : blocks;
+  return blocks > 16384 ? 16384 : blocks;   // more chunks in flight (4096: 5-10% slower cold)
 }
 
 }  // namespace

@@ -262,6 +262,17 @@ __device__ __forceinline__ void copy16_to_lds(const i32x4& rsrc, uint32_t voff, 
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
                : "=&s"(saved) : "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
+// The same with the non-temporal hint, for data a kernel reads once: such a
+// copy does not allocate in the caches, so it evicts no dirty lines of other
+// data on its way (measured: requant and weight transpose 19-28% faster
+// with the caches full of dirty lines, level otherwise).
+__device__ __forceinline__ void copy16_to_lds_nt(const i32x4& rsrc, uint32_t voff, uint32_t soff,
+                                                 uint32_t lds_addr) {
+  uint32_t saved;
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);  // uniform by contract
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen nt lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
 __device__ __forceinline__ void copy4_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t soff,
                                              uint32_t lds_addr) {
   uint32_t saved;

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
     const i32x4 rs = make_rsrc(in + t0 * ld_in_bytes + c0 * ELEM, static_cast<uint32_t>(rows * ld_in_bytes));
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      copy16_to_lds(rs, voff[j], 0u, lds_tile + buf * 16384 + (4 * j + wave) * 1024);
+      copy16_to_lds_nt(rs, voff[j], 0u, lds_tile + buf * 16384 + (4 * j + wave) * 1024);
     if (!SRC_BF16 && wave < 2) {
       const i32x4 rss = make_rsrc(s_in + t0 * lds_in + c0 / 128, static_cast<uint32_t>(rows * lds_in * 4));
       copy4_to_lds(rss, static_cast<uint32_t>(64 * wave + lane) * static_cast<uint32_t>(lds_in * 4), 0u,
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void t
     const i32x4 rs = make_rsrc(q + nb * 128 * ldq + kb * 128, 128u * ldq32);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      copy16_to_lds(rs, voff[j], 0u, lds_tile + buf * 16384 + (4 * j + wave) * 1024);
+      copy16_to_lds_nt(rs, voff[j], 0u, lds_tile + buf * 16384 + (4 * j + wave) * 1024);
   };
 
   const int tg = tid & 7;   // rows 16 tg .. 16 tg + 15 of the block
