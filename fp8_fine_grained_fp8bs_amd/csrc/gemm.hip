@@ -228,7 +228,11 @@ __device__ __forceinline__ void load_frag(Frag<C>& f, const uint8_t* stage, cons
 // so the LDS and the load unit see a steady stream instead of a burst
 // after each barrier.  A scheduling barrier after every step keeps that
 // placement.
-constexpr int LAG = 2;
+// LAG is a template parameter of the group: 3 for BF16 or FP32 output with
+// block scales (1-1.5% faster than 2 at 4096 x 18432 x 7168 and on the
+// K = 2048 shapes), 2 for row scales (3 was 3% slower there) and the
+// quantized output (3 spills there).  The promotion order is the same for
+// every lag, so the results are too.
 
 // Read number k of the next group's fragments: B rows, A rows, A scales,
 // then the B scales.
@@ -278,7 +282,7 @@ __device__ __forceinline__ void promote(v4f (&acc)[C::MB][C::NB], const v4f& par
 }
 
 // issue_part(k) issues copy k of the next issue (k < copies).
-template <class C, bool BROW, int COPIES, class IssuePart>
+template <class C, bool BROW, int COPIES, int LAG, class IssuePart>
 __device__ __forceinline__ void pipelined_group(v4f (&acc)[C::MB][C::NB], const Frag<C>& cur,
                                                 Frag<C>& nxt, const uint8_t* stage_n,
                                                 const float* slot_n, int gq_n, int wm, int wn,
@@ -673,7 +677,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs p) {
           }
           const float* slot_n = reinterpret_cast<const float*>(
               lds + C::sc_area() + (((i + 1) / 4) % NSLOT) * SLOT);  // group g + i + 1
-          pipelined_group<C, BROW, COPIES>(
+          pipelined_group<C, BROW, COPIES, (BROW || OUT == kOutFp8) ? 2 : 3>(
               acc, cur, nxt, lds + ((i + 1) % 3) * C::STAGE, slot_n, (i + 1) & 3, wm, wn, lane,
               [&](int k) { issue_part_q(t - gsub, i % 3, q, hb + hl - hsub, hl % NSLOT, k); });
           __builtin_amdgcn_s_waitcnt(waitcnt_vm(COPIES));
