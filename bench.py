@@ -357,7 +357,18 @@ def time_rows(dev, reps=20, warm=3):
     ms = timed("e5m6_dec", lambda: fp8bs.fp8bs_decode_e5m6(ye, xe))
     rows["decode_e5m6"] = {"shape": f"[{T}][{C_in}]", "us": ms * 1e3, "GB/s": b / ms / 1e6,
                            "frac_hbm": b / ms / 1e6 / HBM_PEAK_GBS, "bytes": b}
-    del ye, xe
+    # the weight gradient's 128x1 operand straight from the E5M6 cache (the
+    # decode fused into the re-quantization) against decode + BF16 requant
+    qet, set_ = torch.empty_like(qxt), torch.empty_like(sxt)
+    ms = timed("requant_e5m6", lambda: fp8bs.fp8bs_requant_T_128x1(fp8bs.SRC_E5M6, ye, None, qet, set_))
+    b = T * C_in * (1.5 + 1) + C_in * (T // 128) * 4
+    t_pair = rows["decode_e5m6"]["us"] + rows["requant_T_128x1_bf16"]["us"] * C_in / C_out
+    rows["requant_T_128x1_e5m6"] = {"shape": f"[{T}][{C_in}] E5M6 -> [{C_in}][{T}]", "us": ms * 1e3,
+                                    "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / HBM_PEAK_GBS,
+                                    "bytes": b,
+                                    "speedup_vs_decode_then_requant_bf16": t_pair / (ms * 1e3),
+                                    "pair_note": "decode row plus the BF16 requant row scaled to these columns"}
+    del ye, xe, qet, set_
     ms = timed("wgrad", lambda: fp8bs.fp8bs_gemm(qxt, sxt, qdt, sdt, fp8bs.BSCALE_ROW_1x128, dW, fp8bs.OUT_F32))
     fl = 2.0 * C_in * C_out * T
     rows["gemm_wgrad_row_f32"] = {"shape": f"M{C_in} N{C_out} K{T}", "us": ms * 1e3,
@@ -475,7 +486,8 @@ def time_rows(dev, reps=20, warm=3):
     # every row: median as "us" (the rates above), plus mean and min, all
     # measured after a cache flush
     timer_of = {"requant_T_128x1_fp8": "requant_fp8", "requant_T_128x1_bf16": "requant_bf16",
-                "encode_e5m6": "e5m6_enc", "decode_e5m6": "e5m6_dec", "gemm_wgrad_row_f32": "wgrad",
+                "encode_e5m6": "e5m6_enc", "decode_e5m6": "e5m6_dec", "requant_T_128x1_e5m6": "requant_e5m6",
+                "gemm_wgrad_row_f32": "wgrad",
                 "transpose_w_128x128": "transpose_w", "gemm_dgrad_bf16": "dgrad",
                 "swiglu_quant_1x128": "swiglu_fused"}
     for tag in ("up", "down"):

@@ -213,20 +213,24 @@ fp8bs_status fp8bs_requant_T_128x1(fp8bs_requant_src src, const void* in, const 
                                    int64_t T, int64_t C, int64_t ld_in, int64_t lds_in,
                                    uint8_t* q_out, int64_t ld_out, float* s_out, int64_t lds_out,
                                    void* stream) {
-  if (src != FP8BS_SRC_FP8_1x128 && src != FP8BS_SRC_BF16) return FP8BS_ERR_INVALID_ARG;
+  if (src != FP8BS_SRC_FP8_1x128 && src != FP8BS_SRC_BF16 && src != FP8BS_SRC_E5M6)
+    return FP8BS_ERR_INVALID_ARG;
   if (T < 0 || C <= 0) return FP8BS_ERR_INVALID_ARG;
   if (C % 128 != 0) return FP8BS_ERR_UNSUPPORTED_SHAPE;
   if (T == 0) return FP8BS_OK;
-  const bool bf16 = (src == FP8BS_SRC_BF16);
-  FP8BS_TRY(check_matrix(in, C, ld_in, bf16 ? 2 : 1));
-  if (!bf16) FP8BS_TRY(check_scales(s_in, C / 128, lds_in));
+  const bool codes = (src == FP8BS_SRC_FP8_1x128);
+  // an input row: C codes, C bf16 values, or 1.5 C bytes of E5M6 (ld_in in bytes)
+  const int64_t row_bytes = src == FP8BS_SRC_BF16 ? 2 * C : src == FP8BS_SRC_E5M6 ? C / 2 * 3 : C;
+  const int64_t elem = src == FP8BS_SRC_BF16 ? 2 : 1;
+  FP8BS_TRY(check_matrix(in, row_bytes / elem, ld_in, elem));
+  if (codes) FP8BS_TRY(check_scales(s_in, C / 128, lds_in));
   FP8BS_TRY(check_matrix(q_out, T, ld_out, 1));
   FP8BS_TRY(check_scales(s_out, (T + 127) / 128, lds_out));
   // 128-token tiles are addressed with 32-bit offsets from their first row
-  if (ld_in * (bf16 ? 2 : 1) >= kMaxRequantStride || (!bf16 && lds_in >= kMaxScaleStride))
+  if (ld_in * elem >= kMaxRequantStride || (codes && lds_in >= kMaxScaleStride))
     return FP8BS_ERR_UNSUPPORTED_SHAPE;
   FP8BS_TRY(check_device());
-  return launched(fp8bs::launch_requant_T_128x1(bf16, in, s_in, T, C, ld_in, lds_in, q_out, ld_out,
+  return launched(fp8bs::launch_requant_T_128x1(static_cast<int>(src), in, s_in, T, C, ld_in, lds_in, q_out, ld_out,
                                                 s_out, lds_out, static_cast<hipStream_t>(stream)));
 }
 

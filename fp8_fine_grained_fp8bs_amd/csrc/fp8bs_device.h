@@ -190,6 +190,78 @@ __device__ __forceinline__ uint32_t encode4_bf16(const float v[4], const TileSca
   return encode4(v, t);
 }
 
+// E5M6 (12-bit: sign, 5 exponent bits with bias 15, 6 mantissa bits) to
+// bf16, exact: every E5M6 value is a bf16 value.
+__device__ __forceinline__ uint32_t bf16_of_e5m6(uint32_t c) {
+  const uint32_t sign = (c >> 11) << 15;
+  const uint32_t e = (c >> 6) & 31u, m = c & 63u;
+  uint32_t mag;
+  if (e == 31u) mag = m ? 0x7FC0u : 0x7F80u;
+  else if (e == 0u) mag = __float_as_uint(static_cast<float>(m) * 0x1p-20f) >> 16;  // exact
+  else mag = ((e + 112u) << 7) | (m << 1);
+  return sign | mag;
+}
+
+// Eight packed E5M6 values (96 bits, value i in bits 12 i .. 12 i + 11 of
+// d0 | d1 << 32 | d2 << 64) to eight bf16 values, two per word.
+__device__ __forceinline__ uint4 bf16x8_of_e5m6x8(uint32_t d0, uint32_t d1, uint32_t d2) {
+  const uint32_t code[8] = {d0 & 0xfffu,
+                            (d0 >> 12) & 0xfffu,
+                            (d0 >> 24) | ((d1 & 0xfu) << 8),
+                            (d1 >> 4) & 0xfffu,
+                            (d1 >> 16) & 0xfffu,
+                            (d1 >> 28) | ((d2 & 0xffu) << 4),
+                            (d2 >> 8) & 0xfffu,
+                            d2 >> 20};
+  uint4 o;
+  o.x = bf16_of_e5m6(code[0]) | (bf16_of_e5m6(code[1]) << 16);
+  o.y = bf16_of_e5m6(code[2]) | (bf16_of_e5m6(code[3]) << 16);
+  o.z = bf16_of_e5m6(code[4]) | (bf16_of_e5m6(code[5]) << 16);
+  o.w = bf16_of_e5m6(code[6]) | (bf16_of_e5m6(code[7]) << 16);
+  return o;
+}
+
+// The same eight values through FP16: an E5M6 code is the upper 12 bits of
+// the FP16 encoding of its value (sign, 5-bit exponent with bias 15,
+// subnormals, infinity and NaN alike), so code << 4 is an FP16 pattern.
+// Its FP32 conversion is exact and has at most 7 significant bits, so the
+// upper half of that FP32 is the bf16 value.  About 3 instructions per
+// value, without branches.  Finite codes and infinities give the bit
+// patterns of bf16x8_of_e5m6x8; a NaN code gives a NaN of the code's sign
+// whose payload is not the canonical one (for callers whose contract
+// excludes NaN inputs).
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_of_e5m6x2_f16(uint32_t x) {
+  // x: code 2k in bits 0..11, code 2k + 1 in bits 12..23 (bits above: any)
+  // x << 4 holds code 2k << 4 in its lower half; a 16-bit shift by 4 of the
+  // upper half brings code 2k + 1 (bits 16..27) to bits 20..31
+  const u16x2_t z = __builtin_bit_cast(u16x2_t, x << 4) << u16x2_t{0, 4};
+  const f16x2_t h = __builtin_bit_cast(f16x2_t, z);
+  const float lo = static_cast<float>(h.x), hi = static_cast<float>(h.y);
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);   // upper halves
+}
+__device__ __forceinline__ uint4 bf16x8_of_e5m6x8_f16(uint32_t d0, uint32_t d1, uint32_t d2) {
+  uint4 o;
+  o.x = bf16x2_of_e5m6x2_f16(d0);
+  o.y = bf16x2_of_e5m6x2_f16(__builtin_amdgcn_alignbit(d1, d0, 24));
+  o.z = bf16x2_of_e5m6x2_f16(__builtin_amdgcn_alignbit(d2, d1, 16));
+  o.w = bf16x2_of_e5m6x2_f16(d2 >> 8);
+  return o;
+}
+
+// Two bf16 values with every NaN made the canonical quiet NaN of its sign
+// (0x7FC0 / 0xFFC0).  The NaNs of bf16x2_of_e5m6x2_f16 are quiet, so their
+// magnitudes lie in 0x7FC0..0x7FFF above every other value: a signed 16-bit
+// min with 0x7FC0 clamps the positive ones, an unsigned min with 0xFFC0 the
+// negative ones (0xFFC0..0xFFFF), and no other pattern moves.
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t canonical_nan_bf16x2(uint32_t w) {
+  const i16x2_t a = __builtin_elementwise_min(__builtin_bit_cast(i16x2_t, w), i16x2_t{0x7FC0, 0x7FC0});
+  const u16x2_t b = __builtin_elementwise_min(__builtin_bit_cast(u16x2_t, a), u16x2_t{0xFFC0, 0xFFC0});
+  return __builtin_bit_cast(uint32_t, b);
+}
+
 // Max over the 16 lanes of a DPP row (lanes 16r .. 16r+15) of non-negative
 // floats; every lane of the row gets the result.
 __device__ __forceinline__ float row16_max(float v) {

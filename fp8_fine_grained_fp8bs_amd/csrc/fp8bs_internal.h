@@ -34,7 +34,8 @@ hipError_t launch_encode_e5m6(const uint16_t* x, int64_t T, int64_t C, int64_t l
 hipError_t launch_decode_e5m6(const uint8_t* y, int64_t T, int64_t C, int64_t ldy, uint16_t* x,
                               int64_t ldx, hipStream_t st);
 
-hipError_t launch_requant_T_128x1(bool src_bf16, const void* in, const float* s_in,
+// src: 0 E4M3 codes with 1x128 scales, 1 bf16, 2 packed E5M6
+hipError_t launch_requant_T_128x1(int src, const void* in, const float* s_in,
                                   int64_t T, int64_t C, int64_t ld_in, int64_t lds_in,
                                   uint8_t* q_out, int64_t ld_out, float* s_out,
                                   int64_t lds_out, hipStream_t st);

@@ -38,13 +38,27 @@ namespace {
 // Four 256-thread workgroups per compute unit (the launch's grid assumes
 // them): 4 waves per SIMD, so at most 128 VGPRs per wave.  (Left to itself
 // the FP8-source kernel took 130, which let only three workgroups in.)
-template <bool SRC_BF16>
+// Sources: kSrcFp8 (codes and 1x128 scales), kSrcBf16, kSrcE5m6 (12-bit
+// E5M6 as fp8bs_encode_e5m6 packs it).  An E5M6 tile (128 tokens x 64
+// channels, 96 bytes per token row) is loaded into registers (non-temporal,
+// 12 bytes = 8 values per load) while the previous tile is re-quantized,
+// then decoded to bf16 by way of FP16 (an E5M6 code is the upper 12 bits of
+// the FP16 encoding of its value; about 3 instructions per value against 16
+// for decoding the fields with branches, which made this kernel bound by
+// instruction issue) and written into the bf16 tile layout (swizzle
+// included); from there on it is the bf16 path.  Decoding is exact for
+// finite values, so the result is that of the bf16 source on the decoded
+// rows, without their HBM round trip.
+constexpr int kSrcFp8 = 0, kSrcBf16 = 1, kSrcE5m6 = 2;
+
+template <int SRC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void requant_kernel(const uint8_t* __restrict__ in,
                                                       const float* __restrict__ s_in, int64_t T,
                                                       int64_t ld_in_bytes, int64_t lds_in,
                                                       uint8_t* __restrict__ q_out, int64_t ld_out,
                                                       float* __restrict__ s_out, int64_t lds_out,
                                                       int64_t tiles, int64_t ctiles) {
+  constexpr bool SRC_BF16 = SRC != kSrcFp8;  // the tile in LDS holds bf16 values
   constexpr int ELEM = SRC_BF16 ? 2 : 1;
   constexpr int CW = SRC_BF16 ? 64 : 128;   // channels per tile
   constexpr int CPT = SRC_BF16 ? 2 : 4;     // channels per thread
@@ -86,20 +100,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
     }
   };
 
+  // E5M6 load plan: item j (0..3) of thread tid is token row (tid + 256 j) / 8
+  // of the tile and its 8-channel chunk (tid + 256 j) % 8; E5Regs holds the
+  // 12 words of the four items
+  struct E5Regs {
+    u32x4 a, b, c;
+  };
+  auto e5_load = [&](int64_t t, E5Regs& e) {
+    const int64_t tt = t / ctiles, cb = t - tt * ctiles;
+    const int64_t t0 = tt * 128, c0 = cb * CW;
+    const int rows = static_cast<int>(T - t0 < 128 ? T - t0 : 128);
+    const uint8_t* base = in + t0 * ld_in_bytes + c0 * 3 / 2;
+    uint32_t w[12];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int item = tid + 256 * j, r = item >> 3, c = item & 7;
+      // rows past T are zeros, as the copies of the other sources read them
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(base + (r < rows ? r : 0) * ld_in_bytes + 12 * c);
+      const uint32_t m = r < rows ? 0xffffffffu : 0u;
+      w[3 * j] = __builtin_nontemporal_load(src) & m;
+      w[3 * j + 1] = __builtin_nontemporal_load(src + 1) & m;
+      w[3 * j + 2] = __builtin_nontemporal_load(src + 2) & m;
+    }
+    e.a = u32x4{w[0], w[1], w[2], w[3]};
+    e.b = u32x4{w[4], w[5], w[6], w[7]};
+    e.c = u32x4{w[8], w[9], w[10], w[11]};
+  };
+  auto e5_store = [&](int buf, const E5Regs& e) {
+    const uint32_t w[12] = {e.a[0], e.a[1], e.a[2], e.a[3], e.b[0], e.b[1], e.b[2], e.b[3],
+                            e.c[0], e.c[1], e.c[2], e.c[3]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int item = tid + 256 * j, r = item >> 3, c = item & 7;
+      const uint4 o = bf16x8_of_e5m6x8_f16(w[3 * j], w[3 * j + 1], w[3 * j + 2]);
+      *reinterpret_cast<uint4*>(&tile[buf][r * 128 + ((c ^ (2 * ((r >> 4) & 3))) << 4)]) = o;
+    }
+  };
+
   const int tg = tid & 7;   // tokens 16 tg .. 16 tg + 15
   const int cg = tid >> 3;  // dword cg of every row: channels CPT cg .. CPT cg + CPT - 1
   const int dw = cg ^ (8 * (tg & 3));
 
-  int64_t t = blockIdx.x;
-  if (t < tiles) issue(t, 0);
-  for (int it = 0; t < tiles; ++it) {
-    const int buf = it & 1;
-    const int64_t tn = t + gridDim.x;
-    // tile t has landed in `buf`; every wave is done with the other buffer
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    block_barrier();
-    if (tn < tiles) issue(tn, buf ^ 1);
-
+  // re-quantize tile t, which is in LDS buffer buf, and store its codes and
+  // scales
+  auto requant_tile = [&](int64_t t, int buf) {
     const int64_t tt = t / ctiles, cb = t - tt * ctiles;
     const int64_t t0 = tt * 128, c0 = cb * CW;
     const uint8_t* tb = &tile[buf][0];
@@ -148,6 +192,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
       }
       if (tg == 0) s_out[ch * lds_out + tt] = ts.s;
     }
+  };
+
+  const int64_t step = gridDim.x;
+  int64_t t = blockIdx.x;
+  if (SRC == kSrcE5m6) {
+    // the loads of tile t + step are in flight while tile t is re-quantized;
+    // then they are decoded into the other buffer (a second register set,
+    // loads two tiles ahead, measured no faster)
+    if (t >= tiles) return;
+    E5Regs r;
+    e5_load(t, r);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    e5_store(0, r);
+    for (int it = 0; t < tiles; ++it) {
+      const int buf = it & 1;
+      const int64_t tn = t + step;
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);   // this wave's decoded rows are in LDS
+      block_barrier();                          // tile t is in `buf`; buf ^ 1 is free
+      if (tn < tiles) e5_load(tn, r);
+      requant_tile(t, buf);
+      if (tn < tiles) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        e5_store(buf ^ 1, r);
+      }
+      t = tn;
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    return;
+  }
+
+  if (t < tiles) issue(t, 0);
+  for (int it = 0; t < tiles; ++it) {
+    const int buf = it & 1;
+    const int64_t tn = t + step;
+    // tile t has landed in `buf`; every wave is done with the other buffer
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    block_barrier();
+    if (tn < tiles) issue(tn, buf ^ 1);
+    requant_tile(t, buf);
     t = tn;
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -250,21 +333,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void t
 
 }  // namespace
 
-hipError_t launch_requant_T_128x1(bool src_bf16, const void* in, const float* s_in, int64_t T,
+hipError_t launch_requant_T_128x1(int src, const void* in, const float* s_in, int64_t T,
                                   int64_t C, int64_t ld_in, int64_t lds_in, uint8_t* q_out,
                                   int64_t ld_out, float* s_out, int64_t lds_out, hipStream_t st) {
-  const int64_t CB = src_bf16 ? C / 64 : C / 128;
+  const int64_t CB = src == kSrcFp8 ? C / 128 : C / 64;
   const int64_t TB = (T + 127) / 128;
   const int64_t tiles = CB * TB;
   // four 33 KiB workgroups per compute unit of a 256-CU MI355X
   const int64_t grid = tiles < 1024 ? tiles : 1024;
-  const uint8_t* src = static_cast<const uint8_t*>(in);
-  if (src_bf16)
-    hipLaunchKernelGGL(requant_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, src,
-                       s_in, T, ld_in * 2, lds_in, q_out, ld_out, s_out, lds_out, tiles, CB);
+  const uint8_t* s8 = static_cast<const uint8_t*>(in);
+  const dim3 g(static_cast<unsigned>(grid)), b(256);
+  if (src == kSrcBf16)
+    hipLaunchKernelGGL(requant_kernel<kSrcBf16>, g, b, 0, st, s8, s_in, T, ld_in * 2, lds_in, q_out, ld_out,
+                       s_out, lds_out, tiles, CB);
+  else if (src == kSrcE5m6)
+    hipLaunchKernelGGL(requant_kernel<kSrcE5m6>, g, b, 0, st, s8, s_in, T, ld_in, lds_in, q_out, ld_out,
+                       s_out, lds_out, tiles, CB);
   else
-    hipLaunchKernelGGL(requant_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, src,
-                       s_in, T, ld_in, lds_in, q_out, ld_out, s_out, lds_out, tiles, CB);
+    hipLaunchKernelGGL(requant_kernel<kSrcFp8>, g, b, 0, st, s8, s_in, T, ld_in, lds_in, q_out, ld_out,
+                       s_out, lds_out, tiles, CB);
   return hipGetLastError();
 }
 

@@ -30,6 +30,7 @@ BSCALE_BLOCK_128x128 = 0
 BSCALE_ROW_1x128 = 1
 SRC_FP8_1x128 = 0
 SRC_BF16 = 1
+SRC_E5M6 = 2
 
 ENTRY_POINTS = ("fp8bs_quant_act_1x128", "fp8bs_quant_w_128x128", "fp8bs_quant_act_w",
                 "fp8bs_swiglu_quant_1x128",
@@ -232,13 +233,17 @@ def fp8bs_decode_e5m6(y, x, stream=None):
 
 
 def fp8bs_requant_T_128x1(src, x, s_in, q_out, s_out, stream=None):
-    """x [T][C] (codes with s_in [T][C/128], or bf16) -> q_out [C][T],
-    s_out [C][ceil(T/128)]."""
-    T, C = x.shape
+    """x [T][C] (codes with s_in [T][C/128], or bf16), or packed E5M6
+    x u8 [T][1.5 C] -> q_out [C][T], s_out [C][ceil(T/128)]."""
+    if int(src) == SRC_E5M6:
+        T, C = x.shape[0], q_out.shape[0]
+        _check(x, "x", (T, C // 2 * 3), _CODES)
+    else:
+        T, C = x.shape
     if int(src) == SRC_FP8_1x128:
         _check(x, "x", (T, C), _CODES)
         _check(s_in, "s_in", (T, (">=", _groups(C))), ("float32",))
-    else:
+    elif int(src) == SRC_BF16:
         _check(x, "x", (T, C), ("bfloat16",))
     _check(q_out, "q_out", (C, T), _CODES)
     _check(s_out, "s_out", (C, (">=", (T + 127) // 128)), ("float32",))
@@ -436,6 +441,17 @@ def requant_T_128x1(x, s_in=None, stream=None):
     s = torch.empty((C, (T + 127) // 128), dtype=torch.float32, device=x.device)
     src = SRC_FP8_1x128 if s_in is not None else SRC_BF16
     fp8bs_requant_T_128x1(src, x, s_in, q, s, stream)
+    return q, s
+
+
+def requant_T_128x1_e5m6(y, C, stream=None):
+    """Packed E5M6 rows y u8 [T][1.5 C] -> (q [C][T], s [C][ceil(T/128)])."""
+    import torch
+    T = y.shape[0]
+    Tp = (T + 15) // 16 * 16  # 16-byte aligned output rows
+    q = torch.empty((C, Tp), dtype=torch.uint8, device=y.device)[:, :T]
+    s = torch.empty((C, (T + 127) // 128), dtype=torch.float32, device=y.device)
+    fp8bs_requant_T_128x1(SRC_E5M6, y, None, q, s, stream)
     return q, s
 
 

@@ -61,7 +61,8 @@ typedef enum {
 
 typedef enum {
     FP8BS_SRC_FP8_1x128 = 0,        /* E4M3 codes with 1x128 scales */
-    FP8BS_SRC_BF16 = 1              /* plain bf16 */
+    FP8BS_SRC_BF16 = 1,             /* plain bf16 */
+    FP8BS_SRC_E5M6 = 2              /* 12-bit E5M6 rows as fp8bs_encode_e5m6 packs them */
 } fp8bs_requant_src;
 
 /*
@@ -147,8 +148,9 @@ fp8bs_status fp8bs_cast_e4m3(const float *x, int64_t n, uint8_t *q, void *stream
  * bits 12 i .. 12 i + 11, little-endian.
  * Encoding rounds each bf16 value to the nearest E5M6 value, ties to the
  * even mantissa, magnitudes from 65280 up to infinity (IEEE overflow).
- * Every E5M6 value is a bf16 value, so decoding is exact; the decoded rows
- * feed fp8bs_requant_T_128x1 with FP8BS_SRC_BF16 in the backward pass.
+ * Every E5M6 value is a bf16 value, so decoding is exact; in the backward
+ * pass fp8bs_requant_T_128x1 takes the packed rows directly (FP8BS_SRC_E5M6),
+ * with the result it gives for the decoded rows as FP8BS_SRC_BF16.
  *   x  bf16 [T][ldx]     y  u8 [T][ldy]  (ldy in bytes, >= 1.5 C)
  * T >= 0 (0 is a no-op), C > 0, C % 128 == 0, else
  * FP8BS_ERR_UNSUPPORTED_SHAPE; 16-byte alignment as for every byte buffer.
@@ -190,11 +192,15 @@ fp8bs_status fp8bs_swiglu_quant_1x128(const void *g, int64_t ldg, const void *u,
  * from 1x128 to 128x1; [p1] para 4: activations are cached in FP8 for the
  * backward pass of the Linear operator.
  * Reading: v = fl32(dec(q_in[t][c]) * s_in[t][c/128]) (one FP32 multiply);
- * for src == FP8BS_SRC_BF16, v = x[t][c] and s_in is ignored (may be NULL).
+ * for src == FP8BS_SRC_BF16, v = x[t][c] and s_in is ignored (may be NULL);
+ * for src == FP8BS_SRC_E5M6 ([p1] para 3: E5M6 for activations cached for
+ * the backward pass), v = the E5M6 value packed at x[t][1.5 c] (ld_in in
+ * bytes; decoding is exact, so the result is that of FP8BS_SRC_BF16 on the
+ * decoded rows, without their round trip through HBM) and s_in is ignored.
  * Each run of 128 consecutive tokens t of one channel c is a tile; the
  * result is written channel-major so that T becomes the contiguous (K)
  * dimension of a following GEMM.
- *   in     u8 [T][ld_in] (codes) or bf16 [T][ld_in]
+ *   in     u8 [T][ld_in] (codes), bf16 [T][ld_in], or u8 [T][ld_in] (E5M6, >= 1.5 C bytes)
  *   s_in   f32 [T][lds_in]            s_in[t*lds_in + c/128]
  *   q_out  u8  [C][ld_out]            q_out[c*ld_out + t]
  *   s_out  f32 [C][lds_out]           s_out[c*lds_out + t/128], ceil(T/128) per row

@@ -243,6 +243,14 @@ def requant_T_128x1_bf16(x_bf16: np.ndarray):
     return qo, so
 
 
+def requant_T_128x1_e5m6(y_packed: np.ndarray, C: int):
+    """128x1 re-quantization of E5M6-cached activations ([p1] para 3: E5M6
+    for some activations cached for the backward pass): the exact E5M6
+    decode followed by the bf16-source re-quantization, composed as
+    written (decode_e5m6, then requant_T_128x1_bf16)."""
+    return requant_T_128x1_bf16(decode_e5m6(y_packed, C))
+
+
 def transpose_w_128x128(q_in: np.ndarray, s_in: np.ndarray):
     """Quantized W^T for the backward pass for the input ([p3] para 4 splits
     the backward pass into the input and the weight parts; blocks of [p1]

@@ -166,6 +166,12 @@ def grouped(a=A, sa=A, ldsa=2, b=A, sb=A, off=A, E=2, M=10, d=A, dt=0, N=128, K=
     (lambda: requant(ld_out=264), fp8bs.ERR_MISALIGNED),
     (lambda: requant(ld_in=1 << 25), fp8bs.ERR_UNSUPPORTED_SHAPE),
     (lambda: requant(T=0), fp8bs.OK),
+    (lambda: requant(src=3), fp8bs.ERR_INVALID_ARG),
+    (lambda: requant(src=2, s_in=NULL, ld_in=176), fp8bs.ERR_INVALID_ARG),   # E5M6 rows: 1.5 C bytes
+    (lambda: requant(src=2, s_in=NULL, ld_in=200), fp8bs.ERR_MISALIGNED),
+    (lambda: requant(src=2, s_in=NULL, C=192, ld_in=288), fp8bs.ERR_UNSUPPORTED_SHAPE),
+    (lambda: requant(src=2, x=NULL, s_in=NULL, ld_in=192), fp8bs.ERR_INVALID_ARG),
+    (lambda: requant(src=2, s_in=NULL, ld_in=1 << 25), fp8bs.ERR_UNSUPPORTED_SHAPE),
     (lambda: transpose_w(N=-128), fp8bs.ERR_INVALID_ARG),
     (lambda: transpose_w(K=0), fp8bs.ERR_INVALID_ARG),
     (lambda: transpose_w(N=200, ldqt=208), fp8bs.ERR_UNSUPPORTED_SHAPE),
@@ -262,6 +268,7 @@ def test_valid_call_without_gpu_reports_no_device():
     assert transpose_w() == fp8bs.ERR_NO_DEVICE
     assert quant_pt() == fp8bs.ERR_NO_DEVICE
     assert enc6() == fp8bs.ERR_NO_DEVICE and dec6() == fp8bs.ERR_NO_DEVICE
+    assert requant(src=2, s_in=NULL, ld_in=192) == fp8bs.ERR_NO_DEVICE   # E5M6 source, no scales
     assert gemm_quant() == fp8bs.ERR_NO_DEVICE
     assert gemm() == fp8bs.ERR_NO_DEVICE
 

@@ -52,6 +52,42 @@ def test_e5m6_every_finite_bf16_value():
     assert np.array_equal(back, oracle.decode_e5m6(ref, 128))
 
 
+def _pack_codes(codes):
+    """12-bit codes [T][C] -> packed rows (value i in bits 12 i .. 12 i + 11)."""
+    T, C = codes.shape
+    c = codes.astype(np.uint16)
+    y = np.empty((T, C // 2 * 3), np.uint8)
+    y[:, 0::3] = (c[:, 0::2] & 0xFF).astype(np.uint8)
+    y[:, 1::3] = ((c[:, 0::2] >> 8) | ((c[:, 1::2] & 0xF) << 4)).astype(np.uint8)
+    y[:, 2::3] = (c[:, 1::2] >> 4).astype(np.uint8)
+    return y
+
+
+def test_e5m6_decode_every_code():
+    """All 4096 codes, NaN codes with every payload and both signs included:
+    the oracle's bf16 patterns bit for bit (a NaN code decodes to the quiet
+    NaN 0x7FC0 of its sign), in two orders so every code sits at every
+    position of an 8-value group."""
+    native_loaded()
+    codes = np.arange(4096, dtype=np.uint16).reshape(32, 128)
+    # the helper packs as the oracle's encoder does (rows of finite codes)
+    fin = ~(((codes >> 6) & 31) == 31).any(axis=1)
+    y = _pack_codes(codes)
+    assert np.array_equal(oracle.encode_e5m6(oracle.decode_e5m6(y, 128))[fin], y[fin])
+    for shift in (0, 3):
+        c = np.roll(codes.ravel(), shift).reshape(32, 128)
+        y = _pack_codes(c)
+        announce(f"e5m6 decode, every code, shift {shift}")
+        got = _decode_dev(y, 128, pad_x=8)
+        ref = oracle.decode_e5m6(y, 128)
+        bad = np.flatnonzero(got != ref)
+        assert bad.size == 0, (f"{bad.size} values differ, first code {int(c.ravel()[bad[0]]):#05x}: "
+                               f"{int(got.ravel()[bad[0]]):#06x} vs {int(ref.ravel()[bad[0]]):#06x}")
+    nan = ((codes >> 6) & 31 == 31) & (codes & 63 != 0)
+    ref = oracle.decode_e5m6(_pack_codes(codes), 128)
+    assert set(np.unique(ref[nan])) == {0x7FC0, 0xFFC0}
+
+
 def test_e5m6_backward_shape_and_requant_of_decoded_rows():
     """X [8192][7168] cached in E5M6, decoded, re-quantized to 128x1 tiles:
     every step bit-exact against the oracle."""

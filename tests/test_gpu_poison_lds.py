@@ -5,7 +5,7 @@ kernel that reads LDS it has not written (a missing wait or barrier, a
 stage read before its copy, an unwritten tail) would then produce NaNs or
 wrong codes.  These parity cases run through that build and must still
 match the oracle exactly as the library build does: ragged and strided
-shapes, both B-scale modes, every output form, requant from both sources,
+shapes, both B-scale modes, every output form, requant from every source,
 the weight transpose, the grouped GEMM with empty experts, the BF16-A GEMM
 (A quantized in place in LDS) and the one-launch activation and weight
 quantizer.
@@ -92,6 +92,19 @@ def test_requant_poisoned(T):
     check_quant_equal(f"poisoned requant fp8 T={T}", q, s, *oracle.requant_T_128x1_fp8(q1, s1))
     q, s = _run_requant(d["dY"], ld_in_pad=8, ld_out_pad=32, lds_out_pad=1)
     check_quant_equal(f"poisoned requant bf16 T={T}", q, s, *oracle.requant_T_128x1_bf16(d["dY"]))
+
+
+@pytest.mark.parametrize("T", [256, 300])
+def test_requant_e5m6_poisoned(T):
+    """The E5M6 source writes its decoded rows into LDS itself (no copies):
+    every read of the tile must follow those writes and the barrier."""
+    from tests.test_gpu_requant_e5m6 import run_requant_e5m6
+    native_loaded()
+    x = synth.wgrad(T=T, C_in=384, C_out=128, seed=T + 3)["X"]
+    y = oracle.encode_e5m6(x)
+    announce(f"poisoned requant e5m6 T={T}")
+    q, s = run_requant_e5m6(y, 384, ld_in_pad=16, ld_out_pad=16, lds_out_pad=2)
+    check_quant_equal(f"poisoned requant e5m6 T={T}", q, s, *oracle.requant_T_128x1_e5m6(y, 384))
 
 
 def test_transpose_and_quant_w_poisoned():
