@@ -163,3 +163,26 @@ def test_stream_thin_m(M):
         fb, pb = _bits(full[:, n0:n1]), _bits(part)
         assert (fb == pb).all(), f"thin M={M}: columns {n0}..{n1}: {(fb != pb).sum()} entries differ"
     sampled_check(f"stream thin M={M}", qa, sa, qb, sb, full)
+
+
+@pytest.mark.parametrize("offsets", [[0, 300, 100, 5000, -7, 1000], [0, 1000, 0, 1000, 0, 1000], [0, 0, 0, 0, 0, 0]])
+def test_grouped_inconsistent_offsets_stay_in_bounds(offsets):
+    """Offsets that decrease, overlap, or leave [0, M]: the kernel clamps
+    every expert's rows into [0, M] (and its own tile count to the launch's
+    bound), so the rows it writes are wrong at worst; a guard region past
+    the output keeps its values, and consistent rows of the same launch
+    shape still compute."""
+    native_loaded()
+    M, N, K = 1000, 512, 256
+    E = len(offsets) - 1
+    rng = np.random.default_rng(500)
+    qa = _codes(rng, (M, K))
+    sa = rng.uniform(0.5, 1.5, (M, K // 128)).astype(np.float32)
+    qb = _codes(rng, (E, N, K))
+    sb = rng.uniform(0.5, 1.5, (E, N // 128, K // 128)).astype(np.float32)
+    announce(f"grouped inconsistent offsets {offsets}")
+    guard = torch.full((M + 64, N), 7.0, dtype=torch.float32, device=dev())
+    off = torch.tensor(offsets, dtype=torch.int32, device=dev())
+    fp8bs.fp8bs_grouped_gemm(_dev(qa), _dev(sa), _dev(qb), _dev(sb), off, guard[:M], fp8bs.OUT_F32)
+    g = host(guard)
+    assert (g[M:] == 7.0).all(), "wrote past the output rows"
