@@ -32,8 +32,9 @@
 //   random BF16 data such brackets differ for about 0.5 % of the values
 //   (amax significands with small odd factors), i.e. in most waves.
 //
-// Scales: s = amax / 448 as an IEEE binary32 division (the library is built
-// without fast-math and keeps FP32 subnormals).
+// Scales: s = fl32(amax / 448), the correctly rounded quotient (div448, or
+// the IEEE binary32 division where that does not apply; the library is
+// built without fast-math and keeps FP32 subnormals).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -78,10 +79,26 @@ struct TileScale {
   bool fast;  // s >= 2^-100
 };
 
+// fl32(a / 448) in three operations: q0 = a * fl32(1/448), the exact
+// remainder a - 448 q0 (one FMA), q0 corrected by remainder * fl32(1/448).
+// Equal to the IEEE quotient for every binary32 a whose quotient is at
+// least 2^-100 (checked on the CPU over every significand in exact integer
+// arithmetic, tests/test_div448.py); smaller or non-finite quotients need
+// the IEEE division.
+__device__ __forceinline__ float div448(float a) {
+  constexpr float kInv448 = 1.0f / 448.0f;
+  const float q0 = a * kInv448;
+  const float r = __builtin_fmaf(-q0, 448.0f, a);
+  return __builtin_fmaf(r, kInv448, q0);
+}
+
 __device__ __forceinline__ TileScale make_tile_scale(float amax) {
   TileScale t;
-  t.s = amax / kE4M3Max;
+  t.s = div448(amax);
   t.fast = t.s >= kFastScaleMin;
+  // below 2^-100 (and for zero or a non-finite amax) the IEEE division,
+  // branched around: it is eleven instructions against div448's three
+  if (__builtin_expect(!t.fast, 0)) t.s = amax / kE4M3Max;
   const float r = __builtin_amdgcn_rcpf(t.fast ? t.s : 1.0f);
   t.rlo = r * kMarginLo;
   t.rhi = r * kMarginHi;

@@ -74,19 +74,6 @@ __device__ __forceinline__ v4f mfma_16x16x128_fp8(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
-// fl32(a / 448) in three operations: q0 = a * fl32(1/448), the exact
-// remainder a - 448 q0 (one FMA), q0 corrected by remainder * fl32(1/448).
-// Equal to the IEEE quotient for every BF16 value a whose quotient is at
-// least 2^-100 (checked exhaustively over all of them on the CPU in
-// tests/test_div448.py); smaller or non-finite quotients take the exact
-// path below.
-__device__ __forceinline__ float div448(float a) {
-  constexpr float kInv448 = 1.0f / 448.0f;
-  const float q0 = a * kInv448;
-  const float r = __builtin_fmaf(-q0, 448.0f, a);
-  return __builtin_fmaf(r, kInv448, q0);
-}
-
 // Max over the 16 lanes of a DPP row of non-negative floats (as integers);
 // the row moves feed the max directly.
 __device__ __forceinline__ int row16_imax(int x) {
