@@ -21,9 +21,13 @@ namespace {
 
 // Tile: 128 tokens x CW channels (CW = 128 for FP8 codes, 64 for bf16, so
 // a token row of the tile is 128 bytes either way).  Workgroups are
-// persistent: each walks the tiles blockIdx.x, + gridDim.x, ... with two LDS
-// buffers, and the load unit copies the next tile (and its 128 input
-// scales) global -> LDS directly while the current tile is re-quantized.
+// persistent: each walks the tiles blockIdx.x, + gridDim.x, ...  The FP8
+// source keeps two LDS buffers: the load unit copies the next tile (and its
+// 128 input scales) global -> LDS directly while the current tile is
+// re-quantized.  The bf16 and E5M6 sources keep one (16 KiB), which lets six
+// workgroups share a compute unit instead of four: their loads overlap
+// across workgroups instead of inside one (measured 3-8% faster cold; the
+// FP8 source would spill at six waves per SIMD).
 // Copies are bounded by buffer descriptors, so token rows past T read as
 // zeros.  16-byte chunks of a token row are XOR-swizzled by
 // 2 * ((row / 16) % 4), so that the column reads below see at most 2-way
@@ -35,14 +39,14 @@ namespace {
 // reduction over the 8 lanes that share the channel (DPP), each thread
 // derives the scales of only its own CPT channels, and each channel's 16
 // codes leave as one 16-byte store.
-// Four 256-thread workgroups per compute unit (the launch's grid assumes
-// them): 4 waves per SIMD, so at most 128 VGPRs per wave.  (Left to itself
-// the FP8-source kernel took 130, which let only three workgroups in.)
+// FP8 source: four 256-thread workgroups per compute unit (the launch's
+// grid assumes them): 4 waves per SIMD, so at most 128 VGPRs per wave.
+// (Left to itself it took 130, which let only three workgroups in.)  Other
+// sources: six, at most 80 VGPRs.
 // Sources: kSrcFp8 (codes and 1x128 scales), kSrcBf16, kSrcE5m6 (12-bit
 // E5M6 as fp8bs_encode_e5m6 packs it).  An E5M6 tile (128 tokens x 64
 // channels, 96 bytes per token row) is loaded into registers (non-temporal,
-// 12 bytes = 8 values per load) while the previous tile is re-quantized,
-// then decoded to bf16 by way of FP16 (an E5M6 code is the upper 12 bits of
+// 12 bytes = 8 values per load), then decoded to bf16 by way of FP16 (an E5M6 code is the upper 12 bits of
 // the FP16 encoding of its value; about 3 instructions per value against 16
 // for decoding the fields with branches, which made this kernel bound by
 // instruction issue) and written into the bf16 tile layout (swizzle
@@ -52,7 +56,7 @@ namespace {
 constexpr int kSrcFp8 = 0, kSrcBf16 = 1, kSrcE5m6 = 2;
 
 template <int SRC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void requant_kernel(const uint8_t* __restrict__ in,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SRC == kSrcFp8 ? 4 : 6))) void requant_kernel(const uint8_t* __restrict__ in,
                                                       const float* __restrict__ s_in, int64_t T,
                                                       int64_t ld_in_bytes, int64_t lds_in,
                                                       uint8_t* __restrict__ q_out, int64_t ld_out,
@@ -62,8 +66,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
   constexpr int ELEM = SRC_BF16 ? 2 : 1;
   constexpr int CW = SRC_BF16 ? 64 : 128;   // channels per tile
   constexpr int CPT = SRC_BF16 ? 2 : 4;     // channels per thread
-  __shared__ __align__(16) uint8_t tile[2][128 * 128];
-  __shared__ float srow[2][128];
+  constexpr int NB = SRC_BF16 ? 1 : 2;      // LDS tile buffers
+  __shared__ __align__(16) uint8_t tile[NB][128 * 128];
+  __shared__ float srow[NB][128];
   poison_lds<sizeof(tile)>(tile);
   poison_lds<sizeof(srow)>(srow);
 
@@ -196,27 +201,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
 
   const int64_t step = gridDim.x;
   int64_t t = blockIdx.x;
-  if (SRC == kSrcE5m6) {
-    // the loads of tile t + step are in flight while tile t is re-quantized;
-    // then they are decoded into the other buffer (a second register set,
-    // loads two tiles ahead, measured no faster)
-    if (t >= tiles) return;
+  if (NB == 1) {
+    // one buffer: load, re-quantize, and every wave done reading before the
+    // next tile's load writes the buffer
     E5Regs r;
-    e5_load(t, r);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    e5_store(0, r);
-    for (int it = 0; t < tiles; ++it) {
-      const int buf = it & 1;
-      const int64_t tn = t + step;
-      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);   // this wave's decoded rows are in LDS
-      block_barrier();                          // tile t is in `buf`; buf ^ 1 is free
-      if (tn < tiles) e5_load(tn, r);
-      requant_tile(t, buf);
-      if (tn < tiles) {
+    for (; t < tiles; t += step) {
+      if (SRC == kSrcE5m6) {
+        e5_load(t, r);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        e5_store(buf ^ 1, r);
+        e5_store(0, r);
+        __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);   // this wave's decoded rows are in LDS
+      } else {
+        issue(t, 0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       }
-      t = tn;
+      block_barrier();
+      requant_tile(t, 0);
+      block_barrier();
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     return;
@@ -339,8 +340,10 @@ hipError_t launch_requant_T_128x1(int src, const void* in, const float* s_in, in
   const int64_t CB = src == kSrcFp8 ? C / 128 : C / 64;
   const int64_t TB = (T + 127) / 128;
   const int64_t tiles = CB * TB;
-  // four 33 KiB workgroups per compute unit of a 256-CU MI355X
-  const int64_t grid = tiles < 1024 ? tiles : 1024;
+  // four 33 KiB workgroups (FP8 source) or six 16 KiB ones per compute unit
+  // of a 256-CU MI355X
+  const int64_t cap = src == kSrcFp8 ? 1024 : 1536;
+  const int64_t grid = tiles < cap ? tiles : cap;
   const uint8_t* s8 = static_cast<const uint8_t*>(in);
   const dim3 g(static_cast<unsigned>(grid)), b(256);
   if (src == kSrcBf16)
