@@ -54,6 +54,7 @@ namespace {
 // finite values, so the result is that of the bf16 source on the decoded
 // rows, without their HBM round trip.
 constexpr int kSrcFp8 = 0, kSrcBf16 = 1, kSrcE5m6 = 2;
+constexpr int kXcds = 8;   // MI355X: workgroup b runs on XCD b % 8
 
 template <int SRC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SRC == kSrcFp8 ? 4 : 6))) void requant_kernel(const uint8_t* __restrict__ in,
@@ -205,13 +206,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SRC == kSrc
     // one buffer: load, re-quantize, and every wave done reading before the
     // next tile's load writes the buffer
     E5Regs r;
-    for (; t < tiles; t += step) {
+    for (int64_t v = t; v < tiles; v += step) {
       if (SRC == kSrcE5m6) {
+        // E5M6 rows of adjacent channel tiles (96 bytes each) share cache
+        // lines, so each XCD takes one contiguous range of the tiles
+        // (workgroup b runs on XCD b % 8): neighbours run at the same time
+        // in one L2 instead of fetching the shared lines once per XCD
+        const int64_t x = v % kXcds, q = tiles / kXcds, rem = tiles % kXcds;
+        t = x * q + (x < rem ? x : rem) + v / kXcds;
         e5_load(t, r);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         e5_store(0, r);
         __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);   // this wave's decoded rows are in LDS
       } else {
+        t = v;
         issue(t, 0);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       }
