@@ -46,18 +46,19 @@ namespace {
 // Sources: kSrcFp8 (codes and 1x128 scales), kSrcBf16, kSrcE5m6 (12-bit
 // E5M6 as fp8bs_encode_e5m6 packs it).  An E5M6 tile (128 tokens x 64
 // channels, 96 bytes per token row) is loaded into registers (non-temporal,
-// 12 bytes = 8 values per load), then decoded to bf16 by way of FP16 (an E5M6 code is the upper 12 bits of
-// the FP16 encoding of its value; about 3 instructions per value against 16
-// for decoding the fields with branches, which made this kernel bound by
-// instruction issue) and written into the bf16 tile layout (swizzle
-// included); from there on it is the bf16 path.  Decoding is exact for
-// finite values, so the result is that of the bf16 source on the decoded
-// rows, without their HBM round trip.
+// 12 bytes = 8 values per load), then decoded to bf16 by way of FP16 (an
+// E5M6 code is the upper 12 bits of the FP16 encoding of its value; about 3
+// instructions per value against 16 for decoding the fields with branches,
+// which made this kernel bound by instruction issue) and written into the
+// bf16 tile layout (swizzle included); from there on it is the bf16 path.
+// Decoding is exact for finite values, so the result is that of the bf16
+// source on the decoded rows, without their HBM round trip.
 constexpr int kSrcFp8 = 0, kSrcBf16 = 1, kSrcE5m6 = 2;
 constexpr int kXcds = 8;   // MI355X: workgroup b runs on XCD b % 8
 
 template <int SRC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SRC == kSrcFp8 ? 4 : 6))) void requant_kernel(const uint8_t* __restrict__ in,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SRC == kSrcFp8 ? 4 : 6)))
+void requant_kernel(const uint8_t* __restrict__ in,
                                                       const float* __restrict__ s_in, int64_t T,
                                                       int64_t ld_in_bytes, int64_t lds_in,
                                                       uint8_t* __restrict__ q_out, int64_t ld_out,
