@@ -166,6 +166,7 @@ def grouped(a=A, sa=A, ldsa=2, b=A, sb=A, off=A, E=2, M=10, d=A, dt=0, N=128, K=
     (lambda: requant(ld_out=264), fp8bs.ERR_MISALIGNED),
     (lambda: requant(ld_in=1 << 25), fp8bs.ERR_UNSUPPORTED_SHAPE),
     (lambda: requant(T=0), fp8bs.OK),
+    (lambda: requant(src=2, s_in=NULL, ld_in=192, T=0), fp8bs.OK),    # E5M6 source: a no-op too
     (lambda: requant(src=3), fp8bs.ERR_INVALID_ARG),
     (lambda: requant(src=2, s_in=NULL, ld_in=176), fp8bs.ERR_INVALID_ARG),   # E5M6 rows: 1.5 C bytes
     (lambda: requant(src=2, s_in=NULL, ld_in=200), fp8bs.ERR_MISALIGNED),
