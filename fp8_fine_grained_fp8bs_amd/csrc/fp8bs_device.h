@@ -65,8 +65,12 @@ __device__ __forceinline__ float e4m3_dec(uint32_t code) {
 }
 
 // Pack four floats into four E4M3 codes (byte i = value i), hardware RNE.
+// The first conversion writes the low half of its result and keeps the
+// high half of the old value it is given, which the second conversion then
+// overwrites: any old value will do, and a's own bits (a register that dies
+// here) spare the zeroing move a literal 0 would cost.
 __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
   return static_cast<uint32_t>(r);
 }
