@@ -1,8 +1,9 @@
-"""GPU parity of the GEMM's tile stream: a persistent workgroup with more
-than one tile copies its next tile's first scale block and K groups during
-the current tile's last K groups (when the K-group count G is a multiple of
-4 and at least 8), so the stages, scale slots and fragment sets of every
-later tile run at a phase of 0, 4 or 8 groups.
+"""GPU parity of the GEMM's tile stream, tile orders and tile shapes: a
+persistent workgroup with more than one tile copies its next tile's first
+scale block and K groups during the current tile's last K groups (when the
+K-group count G is a multiple of 4 and at least 8), so the stages, scale
+slots and fragment sets of every later tile run at a phase of 0, 4 or 8
+groups.  Small block-scale problems take 128x128 tiles instead of 128x256.
 
 With at most 256 tiles every workgroup runs one tile and no stream is
 involved; each output element goes through the same operations in the
@@ -186,3 +187,31 @@ def test_grouped_inconsistent_offsets_stay_in_bounds(offsets):
     fp8bs.fp8bs_grouped_gemm(_dev(qa), _dev(sa), _dev(qb), _dev(sb), off, guard[:M], fp8bs.OUT_F32)
     g = host(guard)
     assert (g[M:] == 7.0).all(), "wrote past the output rows"
+
+
+@pytest.mark.parametrize("N,K,out", [(576, 128 * 56, "bf16"), (2048, 128 * 16, "f32"), (200, 128 * 9, "bf16")])
+def test_small_tiles_equal_large_tiles(N, K, out):
+    """Block-scale problems whose 128x128 tiles all fit in one round of the
+    256 persistent workgroups run on 128x128 tiles, larger ones on 128x256
+    tiles.  Both compute every element with the same MFMAs and promotions:
+    the rows of a small launch equal, bit for bit, the same rows inside a
+    launch tall enough to take the large tiles."""
+    native_loaded()
+    M = 2048 if N <= 576 else 1024
+    G = K // 128
+    tiles_n = -(-N // 128)
+    assert (M // 128) * tiles_n <= 256, "the small launch must take 128x128 tiles"
+    big_m = 128 * (256 // tiles_n + 1)
+    assert big_m >= M and (big_m // 128) * tiles_n > 256, "the tall launch must take 128x256 tiles"
+    qa, sa, qb, sb = _operands(big_m, N, K, seed=600 + N)
+    announce(f"small vs large tiles {M}x{N}x{K} ({big_m} rows) {out}")
+    a, sa_d, b, sb_d = _dev(qa), _dev(sa), _dev(qb), _dev(sb)
+    small = fp8bs.gemm(a[:M], sa_d[:M], b, sb_d, fp8bs.BSCALE_BLOCK_128x128, out_f32=(out == "f32"))
+    tall = fp8bs.gemm(a, sa_d, b, sb_d, fp8bs.BSCALE_BLOCK_128x128, out_f32=(out == "f32"))
+    fb, pb = _bits(tall[:M]), _bits(small)
+    assert (fb == pb).all(), f"{(fb != pb).sum()} entries differ between the tile shapes"
+    if out == "f32":
+        sampled_check(f"small tiles {M}x{N}x{K}", qa[:M], sa[:M], qb, sb, small)
+    else:
+        d32 = fp8bs.gemm(a[:M], sa_d[:M], b, sb_d, fp8bs.BSCALE_BLOCK_128x128, out_f32=True)
+        sampled_check(f"small tiles {M}x{N}x{K}", qa[:M], sa[:M], qb, sb, d32, small)
