@@ -217,7 +217,7 @@ def cpu_baseline(x_u16, w_u16, M, N, K):
             "seconds_measured": t_qa + t_qw + t_g}
 
 
-def time_quant_split(dev, X, W, qx, sx, qw, sw, reps=20, warm=3):
+def time_quant_split(dev, X, W, qx, sx, qw, sw, reps=50, warm=3):
     """The step's quantization as two launches (quant_act, then quant_w)
     and as one (quant_act_w), each call after a cache flush."""
     import torch
@@ -253,7 +253,7 @@ def time_quant_split(dev, X, W, qx, sx, qw, sw, reps=20, warm=3):
     return out
 
 
-def time_fused(dev, qx, sx, qw, sw, Y, reps=20, warm=3):
+def time_fused(dev, qx, sx, qw, sw, Y, reps=50, warm=3):
     """The up-projection GEMM with its output quantized for the next layer:
     fused into the epilogue, and unfused (BF16 GEMM, then quant_act of Y)."""
     import torch
@@ -297,7 +297,7 @@ def time_fused(dev, qx, sx, qw, sw, Y, reps=20, warm=3):
     }
 
 
-def time_rows(dev, reps=20, warm=3):
+def time_rows(dev, reps=50, warm=3):
     """Re-quantization, wgrad GEMM, weight transpose and input-gradient GEMM, and
     grouped GEMM rows, at their full sizes."""
     import numpy as np
