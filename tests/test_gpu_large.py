@@ -328,3 +328,188 @@ def test_grouped_gemm_weights_past_4_gib():
         announce(f"grouped past 4 GiB expert {e}: rel-fro {fro:.2e} max-err/sum|ab| {worst:.2e}")
     del a, sa, b, sb, d
     _free()
+
+
+def test_transpose_w_past_2_31_elements():
+    """q [2^18][8320] codes (2^31 + 33.5M elements) with their 128x128 block
+    scales: the transpose equals q^T and s^T on every element, and sampled
+    blocks equal the oracle's."""
+    native_loaded()
+    N, K = 1 << 18, 8320
+    G = K // 128
+    announce(f"large: transpose_w {N}x{K}")
+    q = _random_codes(N, K, 28)
+    s = _positive_scales(N // 128, G, 29)
+    qt = torch.empty((K, N), dtype=torch.uint8, device=dev())
+    st = torch.empty((G, N // 128), dtype=torch.float32, device=dev())
+    fp8bs.fp8bs_transpose_w_128x128(q, s, qt, st)
+    torch.cuda.synchronize()
+    for k0 in range(0, K, 1024):   # q^T in slices of 1024 rows of qt
+        assert torch.equal(qt[k0:k0 + 1024], q[:, k0:k0 + 1024].t().contiguous()), f"qt rows {k0}.."
+    assert torch.equal(st, s.t().contiguous())
+    for nb, kb in [(0, 0), (N // 256, G // 2), (N // 128 - 1, G - 1)]:
+        qb = host(q[nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128].contiguous())
+        sbk = host(s[nb:nb + 1, kb:kb + 1].contiguous())
+        q_ref, s_ref = oracle.transpose_w_128x128(qb, sbk)
+        check_quant_equal(f"transpose_w past 2^31, block ({nb}, {kb})",
+                          host(qt[kb * 128:(kb + 1) * 128, nb * 128:(nb + 1) * 128].contiguous()),
+                          host(st[kb:kb + 1, nb:nb + 1].contiguous()), q_ref, s_ref)
+    del q, s, qt, st
+    _free()
+
+
+def test_gemm_quant_output_past_4_gib():
+    """GEMM with its output quantized 1x128: codes [65541][65792] (ld 65808),
+    4.3 GB; K = 128.  Sampled rows follow the fused-output rule against the
+    binary64 oracle GEMM (scales within the GEMM allowance of the tile's
+    max-abs, codes within half an E4M3 step plus the allowance)."""
+    from tests.test_gpu_gemm_quant import _check_against_f64
+    native_loaded()
+    M, N, K = 65541, 65792, 128
+    LD = N + 16
+    announce(f"large: gemm_quant output {M}x{N} (ld {LD}), K {K}")
+    g = torch.Generator(device=dev()).manual_seed(30)
+    xa = torch.randn((M, K), dtype=torch.float32, device=dev(), generator=g).to(torch.bfloat16)
+    xb = (torch.randn((N, K), dtype=torch.float32, device=dev(), generator=g) * 0.05).to(torch.bfloat16)
+    qa = torch.empty((M, K), dtype=torch.uint8, device=dev())
+    sa = torch.empty((M, 1), dtype=torch.float32, device=dev())
+    qb = torch.empty((N, K), dtype=torch.uint8, device=dev())
+    sb = torch.empty(((N + 127) // 128, 1), dtype=torch.float32, device=dev())
+    fp8bs.fp8bs_quant_act_1x128(xa, qa, sa)
+    fp8bs.fp8bs_quant_w_128x128(xb, qb, sb)
+    del xa, xb
+    q = torch.full((M, LD), 0x55, dtype=torch.uint8, device=dev())
+    s = torch.empty((M, N // 128), dtype=torch.float32, device=dev())
+    fp8bs.fp8bs_gemm_quant_1x128(qa, sa, qb, sb, fp8bs.BSCALE_BLOCK_128x128, q[:, :N], s)
+    torch.cuda.synchronize()
+    assert bool((q[:, N:] == 0x55).all()), "wrote into the padding"
+    for r0 in range(0, M, 8192):
+        sl = slice(r0, min(M, r0 + 8192))
+        bad, zero = _max_code_per_tile(q[sl, :N].reshape(-1, N // 128, 128), s[sl])
+        assert zero == 0 and bad == 0, f"rows {sl}: {bad} tiles without a 448 code, {zero} zero scales"
+    rows = np.array([0, 1, M // 2, 65535, 65536, M - 2, M - 1])
+    ri = torch.from_numpy(rows).to(dev())
+    a_h, sa_h = host(qa[ri].contiguous()), host(sa[ri].contiguous())
+    b_h, sb_h = host(qb), host(sb)
+    d_ref = oracle.gemm(a_h, sa_h, b_h, sb_h)
+    mag = gemm_mag(a_h, sa_h, b_h, sb_h)
+    _check_against_f64("gemm_quant past 4 GiB", host(q[ri, :N].contiguous()), host(s[ri].contiguous()), d_ref, mag)
+    del qa, sa, qb, sb, q, s
+    _free()
+
+
+def test_quant_per_tensor_past_2_31_elements():
+    """2^31 + 384 bf16 values with one scale.  Element 0 holds the tensor's
+    largest magnitude (the rest are clamped below it), so the oracle on the
+    sampled elements together with element 0 has the same scale."""
+    native_loaded()
+    n = (1 << 31) + 384
+    announce(f"large: quant_per_tensor n = {n}")
+    g = torch.Generator(device=dev()).manual_seed(31)
+    x = torch.randn((n,), dtype=torch.float32, device=dev(), generator=g).clamp_(-100.0, 100.0).to(torch.bfloat16)
+    x[0] = 300.0
+    _free()
+    q = torch.empty((n,), dtype=torch.uint8, device=dev())
+    s = torch.empty((1,), dtype=torch.float32, device=dev())
+    fp8bs.fp8bs_quant_per_tensor(x, q, s)
+    torch.cuda.synchronize()
+    idx = np.concatenate([np.arange(0, 128), np.arange(1 << 30, (1 << 30) + 128),
+                          np.arange(n - 256, n)])
+    it = torch.from_numpy(idx).to(dev())
+    q_ref, s_ref = oracle.quant_per_tensor(host(x[it].contiguous()))
+    s_gpu = host(s)
+    assert s_gpu.view(np.uint32)[0] == np.float32(s_ref).view(np.uint32), f"scale {s_gpu[0]!r} vs {s_ref!r}"
+    q_gpu = host(q[it].contiguous())
+    bad = np.flatnonzero(q_gpu != q_ref)
+    assert bad.size == 0, f"{bad.size} codes differ, first at element {idx[bad[0]]}"
+    del x, q, s
+    _free()
+
+
+def test_cast_e4m3_past_2_31_elements():
+    """2^31 + 24 FP32 values (8.6 GB) encoded at unit scale; sampled
+    elements against the oracle's encoder."""
+    native_loaded()
+    n = (1 << 31) + 24
+    announce(f"large: cast_e4m3 n = {n}")
+    g = torch.Generator(device=dev()).manual_seed(32)
+    x = torch.randn((n,), dtype=torch.float32, device=dev(), generator=g) * 100.0
+    q = torch.empty((n,), dtype=torch.uint8, device=dev())
+    fp8bs.fp8bs_cast_e4m3(x, q)
+    torch.cuda.synchronize()
+    assert not bool(((q & 0x7F) == 0x7F).any()), "a NaN code for a finite input"
+    rng = np.random.default_rng(33)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 2000), np.arange(n - 40, n), np.arange(0, 8)]))
+    it = torch.from_numpy(idx).to(dev())
+    xs, qs = host(x[it].contiguous()), host(q[it].contiguous())
+    want = np.array([oracle.e4m3_encode(float(v)) for v in xs], np.uint8)
+    bad = np.flatnonzero(qs != want)
+    assert bad.size == 0, f"{bad.size} codes differ, first at element {idx[bad[0]]}: {xs[bad[0]]!r}"
+    del x, q
+    _free()
+
+
+def test_gemm_bf16a_a_past_4_gib():
+    """BF16 A [2^19 + 5][4224] (4.4 GB) quantized inside the GEMM, N = 136,
+    codes stored: stored rows bit-exact against the oracle's 1x128
+    quantizer, D rows within the GEMM tolerance of the oracle GEMM on those
+    codes."""
+    native_loaded()
+    M, N, K = (1 << 19) + 5, 136, 4224
+    G = K // 128
+    announce(f"large: gemm_bf16a {M}x{K}, N {N}")
+    gen = torch.Generator(device=dev()).manual_seed(34)
+    x = torch.randn((M, K), dtype=torch.float32, device=dev(), generator=gen).to(torch.bfloat16)
+    _free()
+    qb = _random_codes(N, K, 35)
+    sb = _positive_scales((N + 127) // 128, G, 36)
+    qx = torch.empty((M, K), dtype=torch.uint8, device=dev())
+    sx = torch.empty((M, G), dtype=torch.float32, device=dev())
+    d = torch.empty((M, N), dtype=torch.float32, device=dev())
+    fp8bs.fp8bs_gemm_bf16a(x, qx, sx, qb, sb, d, fp8bs.OUT_F32)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 63, 64, M // 2, (1 << 19) - 1, 1 << 19, M - 2, M - 1])
+    ri = torch.from_numpy(rows).to(dev())
+    q_ref, s_ref = oracle.quant_act_1x128(host(x[ri].contiguous()))
+    check_quant_equal("gemm_bf16a codes past 4 GiB", host(qx[ri].contiguous()), host(sx[ri].contiguous()),
+                      q_ref, s_ref)
+    b_h, sb_h = host(qb), host(sb)
+    ref = oracle.gemm(q_ref, s_ref, b_h, sb_h)
+    mag = gemm_mag(q_ref, s_ref, b_h, sb_h)
+    fro, worst = check_f32_gemm("gemm_bf16a past 4 GiB", host(d[ri].contiguous()), ref, mag)
+    announce(f"gemm_bf16a past 4 GiB: rel-fro {fro:.2e} max-err/sum|ab| {worst:.2e}")
+    del x, qb, sb, qx, sx, d
+    _free()
+
+
+def test_quant_act_w_past_2_31_elements():
+    """One launch for X [2^19 + 3][4096] (2^31 + 12288 elements) and
+    W [16385][4096]: sampled X rows and the first and last W block rows
+    against the oracle's two quantizers."""
+    native_loaded()
+    M, N, K = (1 << 19) + 3, 16385, 4096
+    G = K // 128
+    announce(f"large: quant_act_w X {M}x{K}, W {N}x{K}")
+    gen = torch.Generator(device=dev()).manual_seed(37)
+    x = torch.randn((M, K), dtype=torch.float32, device=dev(), generator=gen).to(torch.bfloat16)
+    _free()
+    w = (torch.randn((N, K), dtype=torch.float32, device=dev(), generator=gen) * 0.02).to(torch.bfloat16)
+    qx = torch.empty((M, K), dtype=torch.uint8, device=dev())
+    sx = torch.empty((M, G), dtype=torch.float32, device=dev())
+    qw = torch.empty((N, K), dtype=torch.uint8, device=dev())
+    sw = torch.empty(((N + 127) // 128, G), dtype=torch.float32, device=dev())
+    fp8bs.fp8bs_quant_act_w(x, qx, sx, w, qw, sw)
+    torch.cuda.synchronize()
+    bad, zero = _max_code_per_tile(qx.view(M, G, 128), sx)
+    assert zero == 0 and bad == 0, f"{bad} X tiles without a 448 code, {zero} zero scales"
+    rows = np.array([0, 1, M // 2, (1 << 19) - 1, 1 << 19, M - 2, M - 1])
+    ri = torch.from_numpy(rows).to(dev())
+    q_ref, s_ref = oracle.quant_act_1x128(host(x[ri].contiguous()))
+    check_quant_equal("quant_act_w X past 2^31", host(qx[ri].contiguous()), host(sx[ri].contiguous()), q_ref, s_ref)
+    for nb in [0, (N + 127) // 128 - 1]:
+        r0, r1 = nb * 128, min(N, nb * 128 + 128)
+        q_ref, s_ref = oracle.quant_w_128x128(host(w[r0:r1].contiguous()))
+        check_quant_equal(f"quant_act_w W block row {nb}", host(qw[r0:r1].contiguous()),
+                          host(sw[nb:nb + 1].contiguous()), q_ref, s_ref)
+    del x, w, qx, sx, qw, sw
+    _free()
