@@ -102,3 +102,44 @@ def test_fine_grained_vs_per_tensor_accuracy(idx):
     # channels, more for x50 outliers, most for rows four decades apart
     assert f[0] < t[0] and f[2] < gain * t[2], (f, t)
     assert res["BF16 GEMM, FP32 accumulate (CPU)"][0] < f[0]
+
+
+def test_per_tensor_flushes_small_rows_fine_grained_keeps_them():
+    """A case whose outcome follows from the arithmetic, not from measured
+    margins.  A (128 x 256, positive): row 0 in [448, 896), rows 1..127 in
+    [2^-20, 2^-19); W (64 x 256) in [0.5, 1).
+    * Per tensor, s = amax/448 >= 1, so every small value divided by s lies
+      below 2^-19, under half the smallest E4M3 subnormal (2^-10): those
+      rows quantize to zero codes and their GEMM rows are exactly zero, a
+      relative error of exactly 1.
+    * Fine-grained, every tile's values lie within a factor 2 of its
+      max-abs, so they land on normal E4M3 codes with a relative error of
+      at most 2^-4 (half of the 2^-3 spacing); all terms being positive,
+      every output entry is within (1 + 2^-4)^2 - 1 < 0.13 of the exact
+      value, relatively (plus the GEMM's 1e-3 allowance)."""
+    native_loaded()
+    rng = np.random.default_rng(41)
+    a = rng.uniform(1.0, 2.0, (128, 256)) * 2.0 ** -20
+    a[0] = rng.uniform(448.0, 896.0, 256)
+    w = rng.uniform(0.5, 1.0, (64, 256))
+    a16, w16 = synth.bf16_bits(a.astype(np.float32)), synth.bf16_bits(w.astype(np.float32))
+    exact = oracle.gemm_bf16_f64(a16, w16)
+    ad, wd = bf16_dev(a16), bf16_dev(w16)
+    qa, sa = fp8bs.quant_act_1x128(ad)
+    qw, sw = fp8bs.quant_w_128x128(wd)
+    fine = host(fp8bs.gemm(qa, sa, qw, sw, out_f32=True)).astype(np.float64)
+    qat, sat = fp8bs.quant_per_tensor(ad)
+    qwt, swt = fp8bs.quant_per_tensor(wd)
+    sa_b = sat.reshape(1, 1).expand(128, 2).contiguous()
+    sw_b = swt.reshape(1, 1).expand(1, 2).contiguous()
+    tensor = host(fp8bs.gemm(qat, sa_b, qwt, sw_b, out_f32=True)).astype(np.float64)
+    assert float(host(sat)[0]) >= 1.0
+    assert ((host(qat)[1:] & 0x7F) == 0).all(), "small rows must quantize to zero codes per tensor"
+    assert (tensor[1:] == 0.0).all()
+    rel_fine = np.abs(fine - exact) / exact
+    # quantization bound plus the GEMM's own allowance, 1e-3 sum|a||b|,
+    # which is 1e-3 of the exact value when every term is positive
+    bound = (1 + 2.0 ** -4) ** 2 - 1 + 1e-3
+    announce(f"flush case: per-tensor small rows relative error 1.0; fine-grained max entry error "
+             f"{rel_fine.max():.3e} (bound {bound:.4f})")
+    assert rel_fine.max() <= bound
